@@ -1,0 +1,37 @@
+"""Plain fp64 CPU oracle for the tiled attention forward pass.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE. Only the test suite, the graft entry's
+smoke check and the benchmark's CPU-baseline leg may import anything here. The
+HIP library never calls into this package and this package never calls into
+the HIP library; the two share no code, headers, tables or constants. The only
+thing both sides consume is the seeded input generator in ``attn_inputs``,
+which holds no attention arithmetic.
+
+Modules
+  attention  exact two-pass attention (the definition) and the online-softmax
+             recurrence, both fp64
+  fp8        the OCP E4M3FN number format and the per-block / per-tensor
+             quantiser, from the format definition
+  metrics    the error measures used to compare a result with the oracle
+
+Sources (web pages on FlashAttention-3, cited by title and section):
+  [WGC]  "Warp Group Cluster 优化：Flash Attention V3 在 H100 上的 FP8 融合计算实践"
+  [JJ]   "大模型加速-核心网络算子-Flash Attention V3"
+  [YT]   "FlashAttention V3：优化框架吞吐量的关键技术实践"
+
+Every function in this package is pinned by tests in ``tests/test_oracle.py``
+and ``tests/test_fp8_model.py`` against library routines, closed forms,
+invariants and brute force; none is "parity unpinned".
+"""
+from .attention import (allowed_range, attention_two_pass, attention_online,
+                        probabilities, attention_rows)
+from .fp8 import (E4M3_MAX, e4m3_decode_table, e4m3_decode, e4m3_encode,
+                  quantize, dequantize, QUANT_BLOCK_ROWS)
+from .metrics import max_abs, l1_rel, rmse_rel
+
+__all__ = [
+    "allowed_range", "attention_two_pass", "attention_online", "probabilities",
+    "attention_rows", "E4M3_MAX", "e4m3_decode_table", "e4m3_decode",
+    "e4m3_encode", "quantize", "dequantize", "QUANT_BLOCK_ROWS", "max_abs",
+    "l1_rel", "rmse_rel",
+]
