@@ -1,0 +1,142 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) tiled attention forward library.
+ *
+ * The library computes the fused attention forward pass
+ *
+ *     O = softmax(scale * Q K^T + mask) V,   LSE = log sum exp(scale * Q K^T + mask)
+ *
+ * block by block with an online (running max / running sum) softmax, so the
+ * N x N score matrix is never stored. Sources (web pages on FlashAttention-3,
+ * cited by title and section):
+ *   [WGC] "Warp Group Cluster 优化：Flash Attention V3 在 H100 上的 FP8 融合计算实践"
+ *   [JJ]  "大模型加速-核心网络算子-Flash Attention V3"
+ *   [YT]  "FlashAttention V3：优化框架吞吐量的关键技术实践"
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees, copies to the host or synchronises; it keeps no
+ *     state between calls apart from a cache of device properties.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL means
+ *     the default stream) and the call returns before the work finishes.
+ *     Device-side faults surface at the caller's next synchronisation.
+ *   - Tensors are contiguous, row-major [B][H][N][d] (d fastest). bf16 is
+ *     bfloat16 bits, fp8 is OCP E4M3FN bytes (bias 7, max 448, no inf).
+ *   - Every argument is validated before any HIP call; a failed check
+ *     returns a negative ATTN_E_* code and enqueues nothing.
+ *   - B*H*N == 0 is a valid empty problem: nothing is launched and ATTN_OK is
+ *     returned (tensor pointers are then not inspected).
+ *   - Calls are thread-safe. Calls that overlap on one stream run in order;
+ *     calls on different streams writing the same outputs race (caller's
+ *     responsibility).
+ */
+#ifndef MI355_ATTN_H
+#define MI355_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v for attn_fwd. o is always bf16, lse always fp32. */
+typedef enum {
+  ATTN_DTYPE_BF16 = 0,      /* q, k, v bf16; bf16 MFMA contractions                 */
+  ATTN_DTYPE_FP8_E4M3 = 1   /* q, k, v E4M3 codes with per-block descales; fp8 MFMA */
+} attn_dtype;
+
+/* Return codes. */
+enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = -1,      /* a required pointer is NULL                               */
+  ATTN_E_SHAPE = -2,     /* B, H or N negative or beyond the supported maximum        */
+  ATTN_E_HEADDIM = -3,   /* d not in {64, 128}                                        */
+  ATTN_E_DTYPE = -4,     /* unknown dtype, or fp8 descale pointers missing            */
+  ATTN_E_ALIGN = -5,     /* a tensor pointer is not 16-byte aligned (lse: 4-byte)     */
+  ATTN_E_WINDOW = -6,    /* window < -1, or causal not 0/1                            */
+  ATTN_E_ALIAS = -7,     /* an output overlaps an input or another output             */
+  ATTN_E_LAUNCH = -8,    /* the kernel launch failed (no device, bad stream, ...)     */
+  ATTN_E_SCALE = -9      /* scale is not finite                                       */
+};
+
+/* Largest supported sizes (index arithmetic is 64-bit; these bound the grid). */
+#define ATTN_MAX_N (1 << 24)
+#define ATTN_MAX_BH (1 << 24)
+/* Rows per fp8 scaling block, for Q, K and V alike. */
+#define ATTN_FP8_BLOCK_ROWS 128
+
+/*
+ * attn_fwd - fused attention forward.
+ *
+ * Computes, for every batch b, head h and query row i, over the allowed key
+ * set A(i):
+ *   s_ij = scale * <q_i, k_j>  (fp8: scale * dq * dk * <q8_i, k8_j>)
+ *   o_i  = sum_{j in A(i)} softmax_j(s_i) * v_j    (fp8: v_j = v8_j * dv)
+ *   lse_i = ln sum_{j in A(i)} exp(s_ij)           (natural log)
+ * The tiled, online-softmax evaluation follows [WGC] section 2 (local max and
+ * sum per key block, running statistics, rescale of the output) and [JJ]
+ * section 2.4; the fused softmax + mask + matmul follows [YT] section 1.2.
+ *
+ *   q, k, v   [B][H][N][d], bf16 (dtype 0) or E4M3 bytes (dtype 1). Read only.
+ *   o         [B][H][N][d] bf16 output (fp32 accumulation, rounded to nearest
+ *             even at the end: [WGC] section 3).
+ *   lse       [B][H][N] fp32 output, may NOT be NULL.
+ *   B, H, N   batch, heads, sequence length (queries = keys = N).
+ *   d         head dimension, 64 or 128 ([WGC] "适用场景": d = 64 or 128).
+ *   causal    1: key j allowed only if j <= i. 0: no causal cut.
+ *   window    -1: no window. w >= 0: keys with i - w <= j <= i (causal) or
+ *             |i - j| <= w (non-causal): the band of [YT] section 2.1.2, both
+ *             ends inclusive. Key tiles wholly outside the allowed set are
+ *             skipped, never loaded ([YT] section 2.1.2).
+ *   scale     finite multiplier of Q K^T (commonly 1/sqrt(d)); 0 and negative
+ *             values are allowed.
+ *   dtype     attn_dtype.
+ *   descale_q, descale_k, descale_v
+ *             fp8 only (ignored and may be NULL for bf16): fp32
+ *             [B][H][ceil(N/128)] dequantisation factors, one per 128-row block
+ *             of the corresponding tensor, as written by attn_fp8_quantize
+ *             ([WGC] section 3, per-block scaling).
+ *   stream    hipStream_t or NULL.
+ *
+ * A row whose allowed set is empty (impossible with the masks above, since
+ * j = i is always allowed) would get o = 0 and lse = -inf.
+ * Returns ATTN_OK or an ATTN_E_* code.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int d, int causal, int window, float scale,
+             int dtype, const float* descale_q, const float* descale_k,
+             const float* descale_v, void* stream);
+
+/*
+ * attn_fp8_quantize - bf16 -> E4M3 with one scaling factor per 128-row block.
+ *
+ * For each (b, h) and each block of 128 rows (the last block may be shorter):
+ *   amax = max |x| over the block (per_tensor = 1: over the whole tensor)
+ *   r = fp32(448 / amax), descale = fp32(amax / 448); amax == 0 gives r = 1,
+ *   descale = 1
+ *   x8 = E4M3(fp32(x * r)), round to nearest even, saturating at +-448
+ * [WGC] section 3 (dynamic per-block scaling into the range of max 448, fp32
+ * accumulation downstream); the format is [JJ] section 1.5's E4M3.
+ *
+ *   x_bf16    [B][H][N][d] bf16 input. Read only.
+ *   x_fp8     [B][H][N][d] E4M3 output bytes.
+ *   descale   [B][H][ceil(N/128)] fp32 output.
+ *   d         64 or 128.
+ *   per_tensor 0: per-block amax. 1: one amax for the whole tensor, written
+ *             into every descale slot (the naive baseline), so attn_fwd treats
+ *             both modes alike.
+ * The per-tensor mode runs three kernels on `stream` and uses `descale` as its
+ * only scratch; nothing else is allocated. Inputs holding Inf or NaN give
+ * undefined codes. Returns ATTN_OK or an ATTN_E_* code.
+ */
+int attn_fp8_quantize(const void* x_bf16, void* x_fp8, float* descale,
+                      int B, int H, int N, int d, int per_tensor, void* stream);
+
+/* Static, human-readable text for a return code (never NULL). */
+const char* attn_strerror(int code);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355_ATTN_H */

@@ -1,0 +1,135 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+function include/attn.h declares, and rejects every invalid argument with the
+documented code before any HIP call (fake device addresses are never touched).
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import tiled_attention_forward_attn_amd as tafa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+A = 0x10000          # fake, 16-byte aligned device addresses, far apart
+GAP = 1 << 36
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", src, flags=re.M)
+
+
+def header_codes():
+    src = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(ATTN_(?:OK|E_\w+))\s*=\s*(-?\d+)", src)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tafa.LIB_PATH):
+        pytest.fail("libmi355attn.so is not built (run __graft_entry__.build())")
+    return tafa.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == {"attn_fwd", "attn_fp8_quantize", "attn_strerror", "attn_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(tafa.SIGNATURES)
+
+
+def test_version_and_strerror(lib):
+    assert tafa.version() == 10000
+    codes = header_codes()
+    assert codes["ATTN_OK"] == 0
+    texts = {tafa.strerror(c) for c in codes.values()}
+    assert len(texts) == len(codes)              # every code has its own text
+    assert tafa.strerror(12345) == "unknown error code"
+
+
+def fwd_args(**kw):
+    a = dict(q=A, k=A + GAP, v=A + 2 * GAP, o=A + 3 * GAP, lse=A + 4 * GAP, B=2, H=3, N=300, d=128,
+             causal=0, window=-1, scale=0.125, dtype=0, dq=None, dk=None, dv=None, stream=None)
+    a.update(kw)
+    return a
+
+
+def call_fwd(lib, **kw):
+    a = fwd_args(**kw)
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                        a["causal"], a["window"], a["scale"], a["dtype"], a["dq"], a["dk"], a["dv"],
+                        a["stream"])
+
+
+E = header_codes()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), "ATTN_E_SHAPE"), (dict(H=-2), "ATTN_E_SHAPE"), (dict(N=-5), "ATTN_E_SHAPE"),
+    (dict(N=(1 << 24) + 1), "ATTN_E_SHAPE"), (dict(B=1 << 13, H=1 << 12), "ATTN_E_SHAPE"),
+    (dict(d=96), "ATTN_E_HEADDIM"), (dict(d=256), "ATTN_E_HEADDIM"), (dict(d=0), "ATTN_E_HEADDIM"),
+    (dict(dtype=2), "ATTN_E_DTYPE"), (dict(dtype=-1), "ATTN_E_DTYPE"),
+    (dict(q=None), "ATTN_E_NULL"), (dict(k=None), "ATTN_E_NULL"), (dict(v=None), "ATTN_E_NULL"),
+    (dict(o=None), "ATTN_E_NULL"), (dict(lse=None), "ATTN_E_NULL"),
+    (dict(dtype=1), "ATTN_E_NULL"),
+    (dict(dtype=1, dq=A + 5 * GAP, dk=A + 6 * GAP), "ATTN_E_NULL"),
+    (dict(causal=2), "ATTN_E_WINDOW"), (dict(causal=-1), "ATTN_E_WINDOW"),
+    (dict(window=-2), "ATTN_E_WINDOW"),
+    (dict(scale=math.inf), "ATTN_E_SCALE"), (dict(scale=math.nan), "ATTN_E_SCALE"),
+    (dict(q=A + 8), "ATTN_E_ALIGN"), (dict(o=A + 3 * GAP + 4), "ATTN_E_ALIGN"),
+    (dict(lse=A + 4 * GAP + 2), "ATTN_E_ALIGN"),
+    (dict(dtype=1, dq=A + 5 * GAP + 1, dk=A + 6 * GAP, dv=A + 7 * GAP), "ATTN_E_ALIGN"),
+    (dict(o=A), "ATTN_E_ALIAS"), (dict(o=A + GAP + 1024), "ATTN_E_ALIAS"),
+    (dict(lse=A + 2 * GAP + 64), "ATTN_E_ALIAS"), (dict(lse=A + 3 * GAP + 16), "ATTN_E_ALIAS"),
+    (dict(dtype=1, dq=A + 3 * GAP, dk=A + 6 * GAP, dv=A + 7 * GAP), "ATTN_E_ALIAS"),
+])
+def test_attn_fwd_rejects(lib, kw, code):
+    assert call_fwd(lib, **kw) == E[code]
+
+
+def test_attn_fwd_empty_problem_is_ok(lib):
+    for kw in (dict(B=0), dict(H=0), dict(N=0), dict(N=0, q=None, o=None, d=77)):
+        assert call_fwd(lib, **kw) == E["ATTN_OK"]
+
+
+def test_attn_fwd_output_right_after_input_is_not_alias(lib):
+    # q occupies [A, A + 2*3*300*128*2); o starting right after it is legal
+    qbytes = 2 * 3 * 300 * 128 * 2
+    rc = call_fwd(lib, o=A + qbytes + (16 - qbytes % 16) % 16)
+    assert rc != E["ATTN_E_ALIAS"]
+
+
+def call_quant(lib, x=A, x8=A + GAP, ds=A + 2 * GAP, B=2, H=3, N=300, d=128, per_tensor=0):
+    return lib.attn_fp8_quantize(x, x8, ds, B, H, N, d, per_tensor, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), "ATTN_E_SHAPE"), (dict(N=(1 << 24) + 1), "ATTN_E_SHAPE"),
+    (dict(d=32), "ATTN_E_HEADDIM"),
+    (dict(x=None), "ATTN_E_NULL"), (dict(x8=None), "ATTN_E_NULL"), (dict(ds=None), "ATTN_E_NULL"),
+    (dict(per_tensor=2), "ATTN_E_DTYPE"),
+    (dict(x=A + 8), "ATTN_E_ALIGN"), (dict(x8=A + GAP + 4), "ATTN_E_ALIGN"),
+    (dict(ds=A + 2 * GAP + 2), "ATTN_E_ALIGN"),
+    (dict(x8=A + 64), "ATTN_E_ALIAS"), (dict(ds=A + GAP + 128), "ATTN_E_ALIAS"),
+])
+def test_quantize_rejects(lib, kw, code):
+    assert call_quant(lib, **kw) == E[code]
+
+
+def test_quantize_empty_problem_is_ok(lib):
+    assert call_quant(lib, N=0, x=None) == E["ATTN_OK"]
+
+
+def test_binding_checks_before_calling(lib):
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tafa.fwd(q, q, q)                        # CPU tensors are refused by the binding
+    with pytest.raises(ValueError):
+        tafa.quantize(q)

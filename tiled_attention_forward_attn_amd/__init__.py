@@ -1,0 +1,145 @@
+"""Python binding of the MI355X tiled attention forward library.
+
+Argument marshalling only: every step of the attention forward pass and of the
+fp8 quantiser runs in the HIP kernels of libmi355attn.so, reached through its
+C ABI (include/attn.h). PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing or fails to load, every call
+raises.
+
+    o, lse = fwd(q, k, v, causal=False, window=-1, scale=None)      # bf16
+    q8, dq = quantize(q); k8, dk = quantize(k); v8, dv = quantize(v)
+    o, lse = fwd(q8, k8, v8, descales=(dq, dk, dv))                  # fp8
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libmi355attn.so"
+LIB_PATH = os.path.join(_HERE, LIB_NAME)
+BLOCK_ROWS = 128                      # rows per fp8 scaling block
+
+DTYPE_BF16 = 0
+DTYPE_FP8_E4M3 = 1
+
+_lib: ctypes.CDLL | None = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+# name -> (restype, argtypes); mirrors include/attn.h
+SIGNATURES = {
+    "attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp]),
+    "attn_fp8_quantize": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "attn_strerror": (ctypes.c_char_p, [_i]),
+    "attn_version": (_i, []),
+}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what} failed with code {code}: {strerror(code)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libmi355attn.so (built in-tree by build.py); raises if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m tiled_attention_forward_attn_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load().attn_strerror(code).decode()
+
+
+def version() -> int:
+    return load().attn_version()
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_4d(name: str, t: torch.Tensor):
+    if t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 4-D [B, H, N, d] CUDA tensor")
+
+
+def _is_fp8(t: torch.Tensor) -> bool:
+    return t.dtype in (torch.uint8, torch.float8_e4m3fn)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+        window: int = -1, scale: float | None = None, descales=None,
+        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
+    """Attention forward through attn_fwd. Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N]).
+
+    q, k, v: bf16, or E4M3 codes (uint8 / float8_e4m3fn) with
+    descales=(dq, dk, dv) fp32 [B, H, ceil(N/128)]. scale=None means 1/sqrt(d).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_4d(name, t)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must have the same shape")
+    B, H, N, d = q.shape
+    fp8 = _is_fp8(q)
+    if fp8 != _is_fp8(k) or fp8 != _is_fp8(v) or (not fp8 and not (q.dtype == k.dtype == v.dtype == torch.bfloat16)):
+        raise ValueError("q, k, v must all be bf16 or all be E4M3 codes")
+    if fp8 and descales is None:
+        raise ValueError("fp8 inputs need descales=(dq, dk, dv)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = descales if fp8 else (None, None, None)
+    rc = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                         int(causal), int(window), float(scale),
+                         DTYPE_FP8_E4M3 if fp8 else DTYPE_BF16,
+                         _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd")
+    return out, lse
+
+
+def quantize(x: torch.Tensor, per_tensor: bool = False, out: torch.Tensor | None = None,
+             descale: torch.Tensor | None = None, stream=None):
+    """bf16 [B,H,N,d] -> (E4M3 codes uint8 [B,H,N,d], fp32 descale [B,H,ceil(N/128)])."""
+    _check_4d("x", x)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    B, H, N, d = x.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    if descale is None:
+        descale = torch.empty((B, H, -(-N // BLOCK_ROWS)), dtype=torch.float32, device=x.device)
+    rc = load().attn_fp8_quantize(_ptr(x), _ptr(out), _ptr(descale), B, H, N, d,
+                                  int(per_tensor), _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_fp8_quantize")
+    return out, descale
+
+
+__all__ = ["fwd", "quantize", "load", "strerror", "version", "AttnError", "LIB_PATH",
+           "SIGNATURES", "BLOCK_ROWS", "DTYPE_BF16", "DTYPE_FP8_E4M3"]

@@ -1,0 +1,32 @@
+// Internal declarations shared by the HIP translation units of the library.
+// Not part of the public ABI (that is include/attn.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355attn {
+
+// Launch parameters common to the attention kernels, validated by the C ABI.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* dq;   // fp8 descales (nullptr for bf16)
+  const float* dk;
+  const float* dv;
+  int BH;            // B * H
+  int N;
+  int d;
+  int causal;
+  int window;
+  float scale;
+};
+
+hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_fp8(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fp8_quantize(const void* x, void* x8, float* descale, int BH, int N, int d,
+                               int per_tensor, hipStream_t stream);
+
+}  // namespace mi355attn

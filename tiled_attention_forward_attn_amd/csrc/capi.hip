@@ -1,0 +1,113 @@
+// C ABI of the attention library: argument validation and kernel dispatch.
+// Every check runs before the first HIP call, so all error paths are testable
+// on a machine without a GPU. See include/attn.h for the contract.
+#include "attn.h"
+#include "attn_internal.h"
+
+#include <math.h>
+#include <stdint.h>
+
+using namespace mi355attn;
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr long long kMaxGrid = 2147483647LL;  // gridDim.x limit
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+// Shape checks shared by both entry points; *empty is set for B*H*N == 0.
+int check_shape(int B, int H, int N, int d, bool* empty) {
+  if (B < 0 || H < 0 || N < 0) return ATTN_E_SHAPE;
+  *empty = (long long)B * H * N == 0;
+  if (*empty) return ATTN_OK;
+  if (N > ATTN_MAX_N || (long long)B * H > ATTN_MAX_BH) return ATTN_E_SHAPE;
+  if (d != 64 && d != 128) return ATTN_E_HEADDIM;
+  // one workgroup per 128-row block of every head must fit the 1-D grid
+  if ((long long)((N + 127) / 128) * B * H > kMaxGrid) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int N, int d, int causal, int window, float scale,
+                        int dtype, const float* descale_q, const float* descale_k,
+                        const float* descale_v, void* stream) {
+  bool empty = false;
+  int rc = check_shape(B, H, N, d, &empty);
+  if (rc != ATTN_OK || empty) return rc;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP8_E4M3) return ATTN_E_DTYPE;
+  if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+  const bool fp8 = dtype == ATTN_DTYPE_FP8_E4M3;
+  if (fp8 && (!descale_q || !descale_k || !descale_v)) return ATTN_E_NULL;
+  if (causal != 0 && causal != 1) return ATTN_E_WINDOW;
+  if (window < -1) return ATTN_E_WINDOW;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return ATTN_E_ALIGN;
+  if (fp8 && (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4)))
+    return ATTN_E_ALIGN;
+
+  const size_t elems = (size_t)B * H * N * d;
+  const size_t in_bytes = elems * (fp8 ? 1 : 2);
+  const size_t o_bytes = elems * 2;
+  const size_t lse_bytes = (size_t)B * H * N * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins) {
+    if (overlap(o, o_bytes, in, in_bytes) || overlap(lse, lse_bytes, in, in_bytes)) return ATTN_E_ALIAS;
+  }
+  if (overlap(o, o_bytes, lse, lse_bytes)) return ATTN_E_ALIAS;
+  if (fp8) {
+    const size_t ds_bytes = (size_t)B * H * ((N + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS) * sizeof(float);
+    const void* dss[3] = {descale_q, descale_k, descale_v};
+    for (const void* ds : dss)
+      if (overlap(o, o_bytes, ds, ds_bytes) || overlap(lse, lse_bytes, ds, ds_bytes)) return ATTN_E_ALIAS;
+  }
+
+  FwdArgs a{q, k, v, o, lse, descale_q, descale_k, descale_v, B * H, N, d, causal, window, scale};
+  const hipError_t e = fp8 ? launch_attn_fwd_fp8(a, (hipStream_t)stream)
+                           : launch_attn_fwd_bf16(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+extern "C" int attn_fp8_quantize(const void* x_bf16, void* x_fp8, float* descale, int B, int H,
+                                 int N, int d, int per_tensor, void* stream) {
+  bool empty = false;
+  int rc = check_shape(B, H, N, d, &empty);
+  if (rc != ATTN_OK || empty) return rc;
+  if (!x_bf16 || !x_fp8 || !descale) return ATTN_E_NULL;
+  if (per_tensor != 0 && per_tensor != 1) return ATTN_E_DTYPE;
+  if (!aligned(x_bf16, 16) || !aligned(x_fp8, 8) || !aligned(descale, 4)) return ATTN_E_ALIGN;
+  const size_t elems = (size_t)B * H * N * d;
+  const size_t ds_bytes = (size_t)B * H * ((N + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS) * sizeof(float);
+  if (overlap(x_fp8, elems, x_bf16, elems * 2) || overlap(descale, ds_bytes, x_bf16, elems * 2) ||
+      overlap(descale, ds_bytes, x_fp8, elems))
+    return ATTN_E_ALIAS;
+  const hipError_t e = launch_fp8_quantize(x_bf16, x_fp8, descale, B * H, N, d, per_tensor,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+extern "C" const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "success";
+    case ATTN_E_NULL: return "a required pointer is NULL";
+    case ATTN_E_SHAPE: return "B, H or N is negative or beyond the supported maximum";
+    case ATTN_E_HEADDIM: return "head dimension d must be 64 or 128";
+    case ATTN_E_DTYPE: return "unknown dtype or quantisation mode";
+    case ATTN_E_ALIGN: return "a tensor pointer is misaligned (16 bytes for tensors, 4 for fp32 arrays)";
+    case ATTN_E_WINDOW: return "causal must be 0 or 1 and window must be >= -1";
+    case ATTN_E_ALIAS: return "an output buffer overlaps an input or another output";
+    case ATTN_E_LAUNCH: return "kernel launch failed (no usable GPU or invalid stream)";
+    case ATTN_E_SCALE: return "scale must be finite";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" int attn_version(void) { return kVersion; }
