@@ -72,6 +72,24 @@ __device__ __forceinline__ TileRange tile_range(int N, int nqt, int causal, int 
   return t;
 }
 
+// Key tiles [ia, ib) inside [kt0, kt1) are "interior": every key of the tile is
+// allowed for every query of the query tile, so they need no element mask.
+// Tiles before ia and from ib on are "edge" tiles.
+struct InteriorSpan {
+  int ia, ib;
+};
+__device__ __forceinline__ InteriorSpan interior_span(const TileRange& t, int N, int causal,
+                                                      int window) {
+  const int lo_need = window >= 0 ? max(0, t.q_last - window) : 0;   // smallest key all rows allow
+  int hi_need = N;                                                     // one past the largest
+  if (causal) hi_need = min(hi_need, t.q0 + 1);
+  else if (window >= 0) hi_need = min(hi_need, t.q0 + window + 1);
+  InteriorSpan s;
+  s.ia = min(max((lo_need + kBN - 1) / kBN, t.kt0), t.kt1);
+  s.ib = min(max(hi_need / kBN, s.ia), t.kt1);
+  return s;
+}
+
 // True if some (query, key) pair of the key tile starting at k0 is disallowed
 // for some query of the tile (or lies beyond N): only such tiles evaluate the
 // element mask.

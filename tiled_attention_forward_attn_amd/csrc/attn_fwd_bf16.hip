@@ -22,8 +22,9 @@
 //  * K and V tiles are XOR-swizzled in LDS at 16-byte granularity so the
 //    32 rows a wave reads at once fall into distinct banks.
 //  * The online softmax works in base 2 with log2(e) folded into the scale
-//    (v_exp_f32 computes 2^x); the O rescale is skipped when no row max of the
-//    wave moved, which is exact (the factor is exactly 1).
+//    (v_exp_f32 computes 2^x). The reference max of a row only moves when the
+//    row max exceeds it by more than 8 (so p <= 2^8, exact in fp32 and fine in
+//    bf16); the O rescale is skipped unless some row of the wave moved.
 //  * Fully masked key tiles are never visited (causal / sliding-window block
 //    skipping, [YT] section 2.1.2); only tiles straddling a mask edge or the
 //    ragged end of the sequence evaluate the element mask.
@@ -32,6 +33,8 @@
 //    XCD's L2; masked problems issue their heaviest query tiles first.
 #include "attn_device.h"
 #include "attn_internal.h"
+
+#include <type_traits>
 
 namespace mi355attn {
 namespace {
@@ -54,6 +57,10 @@ __device__ __forceinline__ int swz_v(int r) {
     return (r & 3) << 1;
   }
 }
+
+// Slack (base-2 units) by which a row max may exceed the reference max before
+// the reference moves: probabilities reach at most 2^8, fine for bf16.
+constexpr float kRescaleSlack = 8.f;
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2)
@@ -125,7 +132,11 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   }
   __syncthreads();
 
-  for (int kt = kt0; kt < kt1; ++kt) {
+  // One key tile. EDGE tiles evaluate the element mask; interior tiles carry
+  // no mask code at all (the compiler would otherwise if-convert the mask
+  // into every tile).
+  auto step = [&](auto edge_tag, int kt) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int buf = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
     if (more) gload(kt + 1);
@@ -149,8 +160,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // ---- online softmax. sacc[kb][i] is the score of key
     //      k0 + 32 kb + 8 (i/4) + 4 h + i%4 against query qrow.
     const int k0 = kt * kBN;
-    const bool edge = tile_is_edge(tr, k0, N, causal, window);
-    if (edge) {
+    if constexpr (EDGE) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -165,7 +175,12 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
     mx = halves_max(mx);
-    const float mnew = fmaxf(m, mx == -INFINITY ? -INFINITY : mx * c);
+    const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
+    // The reference max only moves when a row max exceeds it by more than
+    // kRescaleSlack (base 2), so p <= 2^kRescaleSlack and the O rescale is
+    // rare; the final O / l and LSE are unchanged mathematically.
+    const bool grow = mxs > m + kRescaleSlack;
+    const float mnew = grow ? mxs : m;
     const float muse = mnew == -INFINITY ? 0.f : mnew;
     const float alpha = fast_exp2(m - muse);
 
@@ -176,15 +191,16 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float p = fast_exp2(fmaf(sacc[kb][i], c, -muse));
-        if (edge) p = sacc[kb][i] == -INFINITY ? 0.f : p;
+        if constexpr (EDGE) p = sacc[kb][i] == -INFINITY ? 0.f : p;
         rs += p;
         pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
       }
-    l = l * alpha + rs;
-    if (__ballot(alpha != 1.f)) {
+    if (__ballot(grow)) {
+      l *= alpha;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
     }
+    l += rs;
     m = mnew;
 
     // ---- O^T += V^T P^T. MFMA step s covers keys 16 s .. 16 s + 15 of the
@@ -209,7 +225,13 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
     if (more) sstore(buf ^ 1);
     __syncthreads();
-  }
+  };
+
+  const InteriorSpan span = interior_span(tr, N, causal, window);
+  int kt = kt0;
+  for (; kt < span.ia; ++kt) step(std::true_type{}, kt);
+  for (; kt < span.ib; ++kt) step(std::false_type{}, kt);
+  for (; kt < kt1; ++kt) step(std::true_type{}, kt);
 
   // ---- epilogue: O = O^T / l (bf16, RNE), LSE = ln 2 * (m + log2 l)
   const float lt = halves_sum(l);

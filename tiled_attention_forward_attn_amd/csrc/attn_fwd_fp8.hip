@@ -21,6 +21,8 @@
 #include "attn_device.h"
 #include "attn_internal.h"
 
+#include <type_traits>
+
 namespace mi355attn {
 namespace {
 
@@ -130,7 +132,9 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
   }
   __syncthreads();
 
-  for (int kt = kt0; kt < kt1; ++kt) {
+  // One key tile; only EDGE tiles carry mask code.
+  auto step = [&](auto edge_tag, int kt) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int buf = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
     if (more) gload(kt + 1);
@@ -158,8 +162,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
     }
 
     // ---- online softmax (identical to the bf16 kernel, per-tile scale c)
-    const bool edge = tile_is_edge(tr, k0, N, causal, window);
-    if (edge) {
+    if constexpr (EDGE) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -190,7 +193,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
         for (int e = 0; e < 4; ++e) {
           const float s = sacc[kb][4 * w + e];
           p[e] = fast_exp2(fmaf(s, c, -muse));
-          if (edge) p[e] = s == -INFINITY ? 0.f : p[e];
+          if constexpr (EDGE) p[e] = s == -INFINITY ? 0.f : p[e];
           rs += p[e];
         }
         pf[4 * kb + w] = cvt4(p[0] * kPScale, p[1] * kPScale, p[2] * kPScale, p[3] * kPScale);
@@ -224,7 +227,13 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
 
     if (more) sstore(buf ^ 1);
     __syncthreads();
-  }
+  };
+
+  const InteriorSpan span = interior_span(tr, N, causal, window);
+  int kt = kt0;
+  for (; kt < span.ia; ++kt) step(std::true_type{}, kt);
+  for (; kt < span.ib; ++kt) step(std::false_type{}, kt);
+  for (; kt < kt1; ++kt) step(std::true_type{}, kt);
 
   // ---- epilogue: O = O_acc * dv_last / (256 l), LSE = ln 2 * (m + log2 l)
   const float lt = halves_sum(l);
