@@ -2,8 +2,11 @@
 
 Tolerances
   bf16 attention: max-abs <= 2e-2 and L1-relative <= 5e-3 over O (the stated
-  bar); LSE max-abs <= 1e-3 (fp32 accumulation of <= 128-term dot products and
-  a base-2 log: observed errors are ~1e-6, the bound leaves room for long rows).
+  bar). LSE max-abs <= 2^-8: the kernel's softmax denominator is the sum of
+  the bf16-rounded probabilities (the same values that weight V), each within
+  2^-9 relative of the exact one, so the sum is within 2^-9 relative and the
+  log within ln(1 + 2^-9) < 2^-9; 2^-8 leaves room for fp32 accumulation and
+  v_exp_f32's last-bit error.
   fp8 quantiser: bit-exact codes and descales (integer output decided in the
   same fp32 steps on both sides).
   fp8 attention vs the oracle on the dequantised inputs: two roundings stand
@@ -38,7 +41,7 @@ pytestmark = pytest.mark.gpu
 
 BF16_MAX_ABS = 2e-2
 BF16_L1_REL = 5e-3
-LSE_MAX_ABS = 1e-3
+LSE_MAX_ABS = 2.0 ** -8
 
 
 def check_bf16(o, lse, ref_o, ref_lse, what=""):

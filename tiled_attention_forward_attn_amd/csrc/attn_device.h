@@ -26,6 +26,43 @@ constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994530942f;
+// Word 3 of a raw buffer resource (no swizzle, 32-bit format field) for gfx950;
+// out-of-range offsets read as zero.
+constexpr int kRsrcWord3 = 0x00020000;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte global -> LDS copy of one lane's chunk: the wave's 64 chunks land
+// contiguously at lds_base + 16 * lane (buffer_load_dwordx4 ... lds).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t res, lds_char* lds_base,
+                                           int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)lds_base, 16, voffset, soffset, 0, 0);
+}
+
+// Raw buffer descriptor (4 dwords: base, base high | stride 0, size in bytes,
+// word 3) over `bytes` bytes at `base`; reads past the size return zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffff), (int)bytes, kRsrcWord3};
+}
+// The same copy issued from inline assembly, so the compiler does not track
+// its LDS write: the callers order it with explicit vmcnt waits and barriers.
+// (The compiler cannot tell that the transposing LDS reads of one tile never
+// touch the tile still being copied, and would otherwise wait for every copy
+// in flight before each of them.) M0 carries the LDS address.
+__device__ __forceinline__ void copy_to_lds16(i32x4 rsrc, const lds_char* lds_base, int voffset,
+                                              int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"((uint32_t)(uintptr_t)lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Bijective remap of the hardware workgroup id so that ids dispatched to the
 // same XCD (w % 8, round-robin dispatch) get consecutive logical ids, i.e. the
@@ -48,6 +85,29 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Max of an array as a tree of v_max3_f32 (short dependency chains).
+template <int N>
+__device__ __forceinline__ float tree_max(const float* x) {
+  if constexpr (N == 1) return x[0];
+  else if constexpr (N == 2) return fmaxf(x[0], x[1]);
+  else if constexpr (N == 3) return fmaxf(fmaxf(x[0], x[1]), x[2]);
+  else {
+    constexpr int T = N / 3;
+    return fmaxf(fmaxf(tree_max<T>(x), tree_max<T>(x + T)), tree_max<N - 2 * T>(x + 2 * T));
+  }
+}
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+// Sum of 8 packed bf16 values (one bf16x8) into fp32 with v_dot2_f32_bf16
+// against (1, 1): products are exact, the additions are fp32.
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[0], v[1]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2], v[3]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[4], v[5]}, one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[6], v[7]}, one, acc, false);
+}
+
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -57,18 +117,20 @@ struct TileRange {
 };
 
 // Masked problems (causal or windowed) visit their heaviest query tiles first.
-__device__ __forceinline__ TileRange tile_range(int N, int nqt, int causal, int window) {
+// bm: query rows per workgroup, bn: keys per key tile.
+__device__ __forceinline__ TileRange tile_range(int N, int nqt, int causal, int window,
+                                                int bm = kBM, int bn = kBN) {
   TileRange t;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   t.bh = logical / nqt;
   const int qt = (causal || window >= 0) ? nqt - 1 - logical % nqt : logical % nqt;
-  t.q0 = qt * kBM;
-  t.q_last = min(N, t.q0 + kBM) - 1;
+  t.q0 = qt * bm;
+  t.q_last = min(N, t.q0 + bm) - 1;
   // allowed keys of the whole query tile: [k_lo, k_hi)
   const int k_lo = window >= 0 ? max(0, t.q0 - window) : 0;
   const int k_hi = causal ? t.q_last + 1 : (window >= 0 ? min(N, t.q_last + window + 1) : N);
-  t.kt0 = k_lo / kBN;
-  t.kt1 = (k_hi + kBN - 1) / kBN;
+  t.kt0 = k_lo / bn;
+  t.kt1 = (k_hi + bn - 1) / bn;
   return t;
 }
 
@@ -79,14 +141,14 @@ struct InteriorSpan {
   int ia, ib;
 };
 __device__ __forceinline__ InteriorSpan interior_span(const TileRange& t, int N, int causal,
-                                                      int window) {
+                                                      int window, int bn = kBN) {
   const int lo_need = window >= 0 ? max(0, t.q_last - window) : 0;   // smallest key all rows allow
   int hi_need = N;                                                     // one past the largest
   if (causal) hi_need = min(hi_need, t.q0 + 1);
   else if (window >= 0) hi_need = min(hi_need, t.q0 + window + 1);
   InteriorSpan s;
-  s.ia = min(max((lo_need + kBN - 1) / kBN, t.kt0), t.kt1);
-  s.ib = min(max(hi_need / kBN, s.ia), t.kt1);
+  s.ia = min(max((lo_need + bn - 1) / bn, t.kt0), t.kt1);
+  s.ib = min(max(hi_need / bn, s.ia), t.kt1);
   return s;
 }
 

@@ -1,43 +1,51 @@
 // Fused attention forward, bf16 inputs, for gfx950 (MI355X / CDNA4).
 //
-// One workgroup of 4 waves owns a 128-row query tile of one (batch, head) and
-// streams the allowed key/value tiles (64 keys each) through LDS, double
-// buffered, so tile j+1's global loads are in flight while tile j is being
-// multiplied. Scores, probabilities and the output accumulator never leave
-// registers; the N x N score matrix is never formed. This is the tiled,
-// fused scheme of [WGC] sections 1-2 (QK^T -> softmax statistics -> PV with
-// running max/sum and output rescale) and [YT] sections 1.2 and 2.1.1
-// (softmax + mask + matmul fused; global tile -> shared-memory tile ->
-// register tile), mapped onto CDNA4 rather than Hopper:
+// A workgroup of 4 waves owns QB x 128 queries of one (batch, head): each
+// wave owns QB blocks of 32 queries. It streams the allowed key/value tiles
+// (BN keys each) through LDS. Scores, probabilities and the output
+// accumulator never leave registers; the N x N score matrix is never formed.
+// This is the tiled, fused scheme of [WGC] sections 1-2 (QK^T -> softmax
+// statistics -> PV with running max/sum and output rescale) and [YT] sections
+// 1.2 and 2.1.1 (softmax + mask + matmul in one kernel; global tile ->
+// shared-memory tile -> register tile), mapped onto CDNA4 rather than Hopper:
 //
-//  * Each wave computes S^T = K Q^T for its 32 queries with
-//    v_mfma_f32_32x32x16_bf16. In the transposed product every lane holds 16
-//    keys of ONE query, so a row's max and sum are in-lane reductions plus a
-//    single v_permlane32_swap with the lane holding the other 16 keys.
-//  * The probabilities come out of the accumulator already in the B-operand
-//    layout of the second product O^T = V^T P^T: P never moves between lanes
-//    and never touches LDS (the register hand-off of [WGC] section 1).
-//  * The V^T operand is read from the row-major V tile with ds_read_b64_tr_b16,
-//    gfx950's transposing LDS read (4 keys x 1 column per lane per read).
-//  * K and V tiles are XOR-swizzled in LDS at 16-byte granularity so the
-//    32 rows a wave reads at once fall into distinct banks.
-//  * The online softmax works in base 2 with log2(e) folded into the scale
-//    (v_exp_f32 computes 2^x). The reference max of a row only moves when the
-//    row max exceeds it by more than 8 (so p <= 2^8, exact in fp32 and fine in
-//    bf16); the O rescale is skipped unless some row of the wave moved.
-//  * Fully masked key tiles are never visited (causal / sliding-window block
-//    skipping, [YT] section 2.1.2); only tiles straddling a mask edge or the
-//    ragged end of the sequence evaluate the element mask.
-//  * Workgroup ids are remapped so that the query tiles of one head land on
-//    one XCD (dispatch is round-robin over the 8 XCDs) and share K/V in that
-//    XCD's L2; masked problems issue their heaviest query tiles first.
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16. In the transposed product each
+//    lane holds 16 keys of ONE query, so a row's max and sum are in-lane
+//    reductions plus one v_permlane32_swap with the lane holding the other 16.
+//  * The probabilities leave the accumulator already in the B-operand layout
+//    of O^T = V^T P^T: P never moves between lanes and never touches LDS (the
+//    register hand-off between the two GEMMs of [WGC] section 1). The V^T
+//    operand is read with ds_read_b64_tr_b16, gfx950's transposing LDS read.
+//  * K and V tiles are copied HBM -> LDS by buffer_load_dwordx4 ... lds (no
+//    staging registers, no LDS write instructions; rows past N read as zero
+//    through the buffer's range check). Tile j+1's K and tile j's V are in
+//    flight while tile j is multiplied (double buffers: [JJ] section 1.2's
+//    ping-pong buffers, [WGC]'s prefetch of the next KV block). The barrier
+//    between tiles carries no memory fence, so those copies stay in flight.
+//  * Software pipeline inside the wave ([JJ] section 2.2, GEMM/softmax
+//    overlap). Iteration j: read all K_j and V_{j-1} fragments of the tile
+//    from LDS up front (their latency hides behind the MFMAs), issue the
+//    MFMAs of S(j) = K_j Q^T, then the MFMAs of O += P(j-1) V_{j-1}
+//    interleaved with the softmax of S(j), so the exponentials run while the
+//    matrix cores are busy. P alternates between two register sets.
+//  * Online softmax in base 2 with log2(e) folded into the scale (v_exp_f32
+//    computes 2^x). A row's reference max only moves when its max exceeds it
+//    by more than 8, so p <= 2^8 and the O rescale (owed to the next
+//    iteration, before its PV) is rare; O / l and the LSE are unchanged.
+//  * Key tiles wholly outside the causal / sliding-window band are never
+//    visited ([YT] section 2.1.2); only tiles straddling the band's edge or the
+//    ragged end of the sequence carry mask code.
+//  * Workgroup ids are remapped so the query tiles of one head land on one XCD
+//    and share K/V in its L2; masked problems issue their heaviest tiles first.
+// The kernel state lives in one struct whose members are all force-inlined, so
+// every array is promoted to registers.
 #include "attn_device.h"
 #include "attn_internal.h"
 
-#include <type_traits>
-
 namespace mi355attn {
 namespace {
+
+constexpr float kRescaleSlack = 8.f;   // see the header comment
 
 // 16-byte chunk swizzles. K is read 16 B per lane from 32 consecutive rows at
 // one chunk column; V is read 8 B per lane as 4 consecutive rows x 32 bytes per
@@ -58,156 +66,70 @@ __device__ __forceinline__ int swz_v(int r) {
   }
 }
 
-// Slack (base-2 units) by which a row max may exceed the reference max before
-// the reference moves: probabilities reach at most 2^8, fine for bf16.
-constexpr float kRescaleSlack = 8.f;
+template <int D, int BN, int QB>
+struct Bf16Fwd {
+  static constexpr int DCH = D / 8;                     // 16-byte chunks per row
+  static constexpr int KSTEPS = D / 16;                 // MFMA k-steps of QK^T
+  static constexpr int DBLK = D / 32;                   // 32-wide d blocks of O^T
+  static constexpr int NKB = BN / 32;                   // 32-key blocks of S^T
+  static constexpr int PST = BN / 16;                   // 16-key MFMA steps of PV
+  static constexpr int TILE = BN * D * 2;               // bytes of one K or V tile
+  static constexpr int LOADS = TILE / (16 * kThreads);  // 16-byte copies per thread
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2)
-void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                          float* __restrict__ LSE, int N, int nqt, float c, int causal,
-                          int window, int qsign) {
-  constexpr int DCH = D / 8;                   // 16-byte chunks per row
-  constexpr int KSTEPS = D / 16;               // MFMA k-steps of QK^T
-  constexpr int DBLK = D / 32;                 // 32-wide d blocks of O^T
-  constexpr int TILE = kBN * D * 2;            // bytes of one K or V tile
-  constexpr int LOADS = kBN * DCH / kThreads;  // 16-byte loads per thread per tile
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K0 K1 V0 V1
-  lds_char* lds = (lds_char*)smem;
+  // problem
+  lds_char* kl[2];   // K stages: K_t lives in stage (t - kt0) & 1
+  lds_char* vl[2];   // V stages, same rule
+  int N, causal, window, kt0, kt1;
+  float c;
+  int lane, wave, h, l32;
+  int qrow[QB];
+  i32x4 kres, vres;                  // buffer descriptors of this head's K and V
+  int koff[LOADS], voff[LOADS];
+  // state
+  bf16x8 qf[QB][KSTEPS];
+  f32x16 oacc[QB][DBLK];
+  f32x16 sacc[QB][NKB];
+  bf16x8 pbuf[2][QB][PST];
+  bf16x8 kf[NKB][KSTEPS];
+  bf16x8 vf[PST][DBLK];
+  float m[QB], l[QB], alpha[QB];
+  bool owe_rescale;
 
-  const TileRange tr = tile_range(N, nqt, causal, window);
-  const int bh = tr.bh, q0 = tr.q0, kt0 = tr.kt0, kt1 = tr.kt1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int qrow = q0 + wave * 32 + l32;
-  const size_t head = (size_t)bh * N * D;
-
-  // Q fragments (B operand of S^T = K Q^T): lane holds q[qrow][16t + 8h .. +7].
-  bf16x8 qf[KSTEPS];
+  template <int ST>
+  __device__ __forceinline__ void issue_k(int kt) {
 #pragma unroll
-  for (int t = 0; t < KSTEPS; ++t) {
-    i32x4 x = {0, 0, 0, 0};
-    if (qrow < N) x = *(const i32x4*)(Q + head + (size_t)qrow * D + 16 * t + 8 * h);
-    x ^= qsign;  // exact sign flip for negative scales
-    qf[t] = __builtin_bit_cast(bf16x8, x);
+    for (int u = 0; u < LOADS; ++u)
+      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff[u], kt * BN * D * 2);
+  }
+  template <int ST>
+  __device__ __forceinline__ void issue_v(int kt) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff[u], kt * BN * D * 2);
   }
 
-  i32x4 kst[LOADS], vst[LOADS];
-  auto gload = [&](int kt) {
+  // A operand of S^T = K Q^T: lane holds K[32 kb + l32][16 t + 8 h .. +7].
+  template <int ST>
+  __device__ __forceinline__ void read_k() {
+    const lds_char* Ks = kl[ST];
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int chunk = tid + u * kThreads;
-      const int row = chunk / DCH, col = chunk % DCH;
-      const int key = kt * kBN + row;
-      if (key < N) {
-        const size_t off = head + (size_t)key * D + col * 8;
-        kst[u] = *(const i32x4*)(K + off);
-        vst[u] = *(const i32x4*)(V + off);
-      } else {
-        kst[u] = i32x4{0, 0, 0, 0};
-        vst[u] = i32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int chunk = tid + u * kThreads;
-      const int row = chunk / DCH, col = chunk % DCH;
-      *(lds_i32x4*)(lds + buf * TILE + row * D * 2 + ((col ^ swz_k<D>(row)) << 4)) = kst[u];
-      *(lds_i32x4*)(lds + (2 + buf) * TILE + row * D * 2 + ((col ^ swz_v<D>(row)) << 4)) = vst[u];
-    }
-  };
-
-  f32x16 oacc[DBLK];
-#pragma unroll
-  for (int db = 0; db < DBLK; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY;  // running max of c * s (base-2 units)
-  float l = 0.f;        // running sum over this lane's 32 keys of each tile
-
-  if (kt0 < kt1) {
-    gload(kt0);
-    sstore(0);
-  }
-  __syncthreads();
-
-  // One key tile. EDGE tiles evaluate the element mask; interior tiles carry
-  // no mask code at all (the compiler would otherwise if-convert the mask
-  // into every tile).
-  auto step = [&](auto edge_tag, int kt) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
-    const int buf = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) gload(kt + 1);
-    const lds_char* Ks = lds + buf * TILE;
-    const lds_char* Vs = lds + (2 + buf) * TILE;
-
-    // ---- S^T = K Q^T for 64 keys x this wave's 32 queries
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) {
       const int row = kb * 32 + l32;
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
         const int ch = 2 * t + h;
-        const bf16x8 kf = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ swz_k<D>(row)) << 4));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sacc[kb], 0, 0, 0);
+        kf[kb][t] = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ swz_k<D>(row)) << 4));
       }
     }
-
-    // ---- online softmax. sacc[kb][i] is the score of key
-    //      k0 + 32 kb + 8 (i/4) + 4 h + i%4 against query qrow.
-    const int k0 = kt * kBN;
-    if constexpr (EDGE) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (!key_allowed(key, qrow, N, causal, window)) sacc[kb][i] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = halves_max(mx);
-    const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
-    // The reference max only moves when a row max exceeds it by more than
-    // kRescaleSlack (base 2), so p <= 2^kRescaleSlack and the O rescale is
-    // rare; the final O / l and LSE are unchanged mathematically.
-    const bool grow = mxs > m + kRescaleSlack;
-    const float mnew = grow ? mxs : m;
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = fast_exp2(m - muse);
-
-    bf16x8 pf[4];
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(sacc[kb][i], c, -muse));
-        if constexpr (EDGE) p = sacc[kb][i] == -INFINITY ? 0.f : p;
-        rs += p;
-        pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
-      }
-    if (__ballot(grow)) {
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
-    }
-    l += rs;
-    m = mnew;
-
-    // ---- O^T += V^T P^T. MFMA step s covers keys 16 s .. 16 s + 15 of the
-    //      tile; lane (d, h) needs V at keys 16s + 4h + {0..3} and + 8.
+  }
+  // A operand of O^T += V^T P^T for MFMA step s: lane (d, h) holds V at keys
+  // 16 s + 4 h + 0..3 and + 8 (the key order of the S^T accumulator).
+  template <int ST>
+  __device__ __forceinline__ void read_v() {
+    const lds_char* Vs = vl[ST];
     const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < PST; ++s) {
       const int r1 = 16 * s + 4 * (g >> 1) + (sl >> 2);
       const int r2 = r1 + 8;
 #pragma unroll
@@ -217,60 +139,281 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         const int a2 = r2 * D * 2 + (((col >> 3) ^ swz_v<D>(r2)) << 4) + ((col >> 2) & 1) * 8;
         const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + a1));
         const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + a2));
-        const bf16x8 va = __builtin_bit_cast(
-            bf16x8, i16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]});
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[s], oacc[db], 0, 0, 0);
+        vf[s][db] = __builtin_bit_cast(bf16x8, i16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1],
+                                                     v2[2], v2[3]});
       }
     }
+  }
 
-    if (more) sstore(buf ^ 1);
-    __syncthreads();
-  };
+  __device__ __forceinline__ void qk() {
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sacc[b][kb] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t)
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+          sacc[b][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][t], qf[b][t], sacc[b][kb], 0, 0, 0);
+  }
 
-  const InteriorSpan span = interior_span(tr, N, causal, window);
-  int kt = kt0;
-  for (; kt < span.ia; ++kt) step(std::true_type{}, kt);
-  for (; kt < span.ib; ++kt) step(std::false_type{}, kt);
-  for (; kt < kt1; ++kt) step(std::true_type{}, kt);
+  template <int PB>
+  __device__ __forceinline__ void pv() {
+#pragma unroll
+    for (int s = 0; s < PST; ++s)
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+          oacc[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s][db], pbuf[PB][b][s], oacc[b][db], 0, 0, 0);
+  }
+
+  // Online softmax of S(kt) into P set PB. sacc[b][kb][i] is the score of key
+  // k0 + 32 kb + 8 (i/4) + 4 h + i%4 against query qrow[b].
+  template <bool EDGE, int PB>
+  __device__ __forceinline__ void softmax(int kt) {
+    const int k0 = kt * BN;
+    bool grow_any = false;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      if constexpr (EDGE) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (!key_allowed(key, qrow[b], N, causal, window)) sacc[b][kb][i] = -INFINITY;
+          }
+      }
+      float sv[16 * NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[16 * kb + i] = sacc[b][kb][i];
+      float mx = tree_max<16 * NKB>(sv);
+      mx = halves_max(mx);
+      const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
+      const bool grow = mxs > m[b] + kRescaleSlack;
+      const float mnew = grow ? mxs : m[b];
+      const float muse = mnew == -INFINITY ? 0.f : mnew;
+      const float a = fast_exp2(m[b] - muse);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(fmaf(sacc[b][kb][i], c, -muse));
+          if constexpr (EDGE) p = sacc[b][kb][i] == -INFINITY ? 0.f : p;
+          pbuf[PB][b][kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
+        }
+      // row sum of the rounded P (the values PV multiplies), 2 per v_dot2
+      float part[PST];
+#pragma unroll
+      for (int st = 0; st < PST; ++st) part[st] = sum_bf16x8(pbuf[PB][b][st], 0.f);
+      float rs = part[0];
+#pragma unroll
+      for (int st = 1; st < PST; ++st) rs += part[st];
+      l[b] = l[b] * a + rs;
+      alpha[b] = a;
+      m[b] = mnew;
+      grow_any = grow_any || grow;
+    }
+    owe_rescale = __ballot(grow_any) != 0;
+  }
+
+  // O *= alpha, owed by the last softmax (rare).
+  __device__ __forceinline__ void rescale() {
+    if (owe_rescale) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) oacc[b][db] *= alpha[b];
+    }
+  }
+
+  // Each wave waits for its own copies (vmcnt), then a barrier without a
+  // memory fence: a fenced barrier would also wait for the copies of the next
+  // tiles, which are meant to stay in flight. Separate LDS objects per stage
+  // let the compiler see that this iteration's LDS reads and the copies in
+  // flight never touch the same memory.
+  __device__ __forceinline__ void sync_tiles() {
+    wait_vmem();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  }
+
+  // Iteration j (stage PB = (j - kt0) & 1): copies of K_{j+1} and V_j go in
+  // flight; S(j) = K_j Q^T; owed rescale; then PV(j-1) interleaved with the
+  // softmax of S(j) into P set PB.
+  template <bool EDGE, int PB, bool FIRST>
+  __device__ __forceinline__ void iteration(int j) {
+    sync_tiles();                           // K_j, V_{j-1} landed; iteration j-1 done
+    // Unconditional (a branch here would make the compiler wait for every
+    // copy at the join): past the last tile it fetches an unused tile, and
+    // rows past N read as zero through the buffer range check.
+    issue_k<PB ^ 1>(j + 1);
+    issue_v<PB>(j);
+    read_k<PB>();
+    if constexpr (!FIRST) read_v<PB ^ 1>();
+    qk();
+    rescale();
+    if constexpr (!FIRST) pv<PB ^ 1>();
+    softmax<EDGE, PB>(j);
+    __builtin_amdgcn_iglp_opt(0);
+  }
+
+  // Tiles [j0, j1) with P set (j - kt0) & 1, unrolled by two so each P set
+  // keeps its registers.
+  template <bool EDGE>
+  __device__ __forceinline__ void run(int j0, int j1) {
+    int j = j0;
+    if (j < j1 && ((j - kt0) & 1)) iteration<EDGE, 1, false>(j++);
+    for (; j + 1 < j1; j += 2) {
+      iteration<EDGE, 0, false>(j);
+      iteration<EDGE, 1, false>(j + 1);
+    }
+    if (j < j1) iteration<EDGE, 0, false>(j);
+  }
+};
+
+template <int D, int BN, int QB>
+__global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1)
+void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                          float* __restrict__ LSE, int N, int nqt, float c, int causal,
+                          int window, int qsign) {
+  using S = Bf16Fwd<D, BN, QB>;
+  constexpr int BMQ = 4 * 32 * QB;
+  __shared__ __attribute__((aligned(1024))) char k0s[S::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[S::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[S::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[S::TILE];
+
+  S st;
+  st.kl[0] = (lds_char*)k0s;
+  st.kl[1] = (lds_char*)k1s;
+  st.vl[0] = (lds_char*)v0s;
+  st.vl[1] = (lds_char*)v1s;
+  const TileRange tr = tile_range(N, nqt, causal, window, BMQ, BN);
+  st.N = N;
+  st.causal = causal;
+  st.window = window;
+  st.kt0 = tr.kt0;
+  st.kt1 = tr.kt1;
+  st.c = c;
+  const int tid = threadIdx.x;
+  st.lane = tid & 63;
+  st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  st.h = st.lane >> 5;
+  st.l32 = st.lane & 31;
+#pragma unroll
+  for (int b = 0; b < QB; ++b) st.qrow[b] = tr.q0 + st.wave * 32 * QB + 32 * b + st.l32;
+  const size_t head = (size_t)tr.bh * N * D;
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds q[qrow][16t + 8h .. +7].
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int t = 0; t < S::KSTEPS; ++t) {
+      i32x4 x = {0, 0, 0, 0};
+      if (st.qrow[b] < N) x = *(const i32x4*)(Q + head + (size_t)st.qrow[b] * D + 16 * t + 8 * st.h);
+      x ^= qsign;  // exact sign flip for negative scales
+      st.qf[b][t] = __builtin_bit_cast(bf16x8, x);
+    }
+
+  // HBM -> LDS copies. Chunk p of a tile's LDS image (16 B, p = 64 * block +
+  // lane) sits at row p / DCH, physical column p % DCH, which holds logical
+  // column (p % DCH) ^ swizzle(row); each lane fetches exactly that chunk.
+  st.kres = make_rsrc(K + head, (uint32_t)N * D * 2);
+  st.vres = make_rsrc(V + head, (uint32_t)N * D * 2);
+#pragma unroll
+  for (int u = 0; u < S::LOADS; ++u) {
+    const int p = (u * 4 + st.wave) * 64 + st.lane;
+    const int row = p / S::DCH, pc = p % S::DCH;
+    st.koff[u] = (row * D + (pc ^ swz_k<D>(row)) * 8) * 2;
+    st.voff[u] = (row * D + (pc ^ swz_v<D>(row)) * 8) * 2;
+  }
+
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+#pragma unroll
+    for (int db = 0; db < S::DBLK; ++db) st.oacc[b][db] = f32x16{};
+    st.m[b] = -INFINITY;   // reference max of c * s (base-2 units)
+    st.l[b] = 0.f;         // running sum over this lane's keys
+    st.alpha[b] = 1.f;
+  }
+  st.owe_rescale = false;
+
+  const int kt0 = tr.kt0, kt1 = tr.kt1;
+  if (kt0 < kt1) {
+    st.template issue_k<0>(kt0);
+    const InteriorSpan span = interior_span(tr, N, causal, window, BN);
+    // the first tile has no PV yet
+    if (kt0 < span.ia || kt0 >= span.ib) st.template iteration<true, 0, true>(kt0);
+    else st.template iteration<false, 0, true>(kt0);
+    const int a = min(max(span.ia, kt0 + 1), kt1), b = min(max(span.ib, a), kt1);
+    st.template run<true>(kt0 + 1, a);
+    st.template run<false>(a, b);
+    st.template run<true>(b, kt1);
+    // drain: PV of the last tile
+    st.sync_tiles();
+    st.rescale();
+    if ((kt1 - 1 - kt0) & 1) {
+      st.template read_v<1>();
+      st.template pv<1>();
+    } else {
+      st.template read_v<0>();
+      st.template pv<0>();
+    }
+  }
 
   // ---- epilogue: O = O^T / l (bf16, RNE), LSE = ln 2 * (m + log2 l)
-  const float lt = halves_sum(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (qrow < N) {
-    uint16_t* orow = O + head + (size_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
+  for (int b = 0; b < QB; ++b) {
+    const float lt = halves_sum(st.l[b]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (st.qrow[b] < N) {
+      uint16_t* orow = O + head + (size_t)st.qrow[b] * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 o4;
+      for (int db = 0; db < S::DBLK; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[db][4 * g4 + e] * inv);
-        *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * h) = o4;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(st.oacc[b][db][4 * g4 + e] * inv);
+          *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * st.h) = o4;
+        }
+      if (st.h == 0) {
+        const float muse = st.m[b] == -INFINITY ? 0.f : st.m[b];
+        LSE[(size_t)tr.bh * N + st.qrow[b]] = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
       }
-    if (h == 0) {
-      const float muse = m == -INFINITY ? 0.f : m;
-      LSE[(size_t)bh * N + qrow] = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
     }
   }
 }
 
+// Configuration per head dimension: queries per wave (32 QB) and keys per tile.
+constexpr int kQB128 = 1, kBN128 = 32;
+constexpr int kQB64 = 1, kBN64 = 64;
+
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  const int nqt = (a.N + kBM - 1) / kBM;
-  const int G = nqt * a.BH;  // bounded by the C ABI's shape checks
   const float c = fabsf(a.scale) * kLog2e;  // |scale| * log2(e)
   const int qsign = a.scale < 0.f ? (int)0x80008000u : 0;
   const uint16_t* q = (const uint16_t*)a.q;
   const uint16_t* k = (const uint16_t*)a.k;
   const uint16_t* v = (const uint16_t*)a.v;
   uint16_t* o = (uint16_t*)a.o;
-  if (a.d == 128)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3(G), dim3(kThreads), 0, stream, q, k, v, o,
-                       a.lse, a.N, nqt, c, a.causal, a.window, qsign);
-  else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3(G), dim3(kThreads), 0, stream, q, k, v, o,
-                       a.lse, a.N, nqt, c, a.causal, a.window, qsign);
+  if (a.d == 128) {
+    const int nqt = (a.N + 128 * kQB128 - 1) / (128 * kQB128);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, kBN128, kQB128>), dim3(nqt * a.BH), dim3(kThreads),
+                       0, stream, q, k, v, o, a.lse, a.N, nqt, c, a.causal, a.window, qsign);
+  } else {
+    const int nqt = (a.N + 128 * kQB64 - 1) / (128 * kQB64);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, kBN64, kQB64>), dim3(nqt * a.BH), dim3(kThreads),
+                       0, stream, q, k, v, o, a.lse, a.N, nqt, c, a.causal, a.window, qsign);
+  }
   return hipGetLastError();
 }
 

@@ -92,7 +92,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
   }
 
   i32x4 kst[LOADS], vst[LOADS];
-  auto gload = [&](int kt) {
+  auto gload = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int chunk = tid + u * kThreads;
@@ -108,7 +108,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
       }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int chunk = tid + u * kThreads;
@@ -133,7 +133,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
   __syncthreads();
 
   // One key tile; only EDGE tiles carry mask code.
-  auto step = [&](auto edge_tag, int kt) {
+  auto step = [&](auto edge_tag, int kt) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     const int buf = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
