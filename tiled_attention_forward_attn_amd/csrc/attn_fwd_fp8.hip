@@ -1,7 +1,7 @@
 // Fused attention forward, E4M3 inputs with per-block descales, for gfx950.
 //
-// Same tiling, online softmax, masking and scheduling as the bf16 kernel
-// (see attn_fwd_bf16.hip), with both contractions on the fp8 matrix cores
+// Same tiling, pipeline, masking and scheduling as the bf16 kernel (see
+// attn_fwd_bf16.hip), with both contractions on the fp8 matrix cores
 // (v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation): [JJ] section 2.3
 // (the forward pass adapted to FP8 GEMMs) and [WGC] section 3 (per-block
 // scaling, FP32 accumulation, BF16 output).
@@ -10,21 +10,28 @@
 //  * a 128-row query tile is exactly one Q scaling block and a 64-key tile
 //    lies inside one K/V scaling block, so the score scale of a tile is the
 //    single number |scale| * log2(e) * dq * dk[block];
-//  * P is converted to E4M3 as p * 2^8 (p <= 1, so p * 256 <= 256 < 448; the
-//    power of two is exact) while the row sum l keeps the unrounded p;
-//  * the output accumulator is kept in units of the current V block's descale:
-//    when the V block changes, the online-softmax rescale factor also carries
-//    dv_old / dv_new, and the epilogue multiplies by dv_last / (256 l).
+//  * P is stored as E4M3(p * 2^8) with an exact running max, so p <= 1 and
+//    the row's largest probability is stored exactly (2^8); with the peaked
+//    softmax of outlier data that one weight is most of the output. The 2^8
+//    is folded into the exp argument; the row sum l is kept in fp32 from the
+//    unrounded p;
+//  * O is kept in units of the current V block's descale: the deferred
+//    rescale that the online softmax owes O also carries dv_old / dv_new
+//    when a tile starts a new V block, and the epilogue multiplies by the
+//    last one. (Folding dv_t / u into P instead would save that rescale but
+//    round the largest weight: measured 6x the kernel error on outlier data
+//    for a 4.5% speed gain.)
 // The V tile is stored in LDS with bits 2 and 3 of each key offset swapped, so
 // that ds_read_b64_tr_b8 (8 consecutive LDS rows of one column per lane) hands
 // every lane exactly the 32 keys whose probabilities it holds in registers.
 #include "attn_device.h"
 #include "attn_internal.h"
 
-#include <type_traits>
-
 namespace mi355attn {
 namespace {
+
+constexpr int kBN8 = 64;               // keys per tile (divides the 128-row scaling block)
+constexpr float kPScaleLog2 = 8.f;     // P is stored as E4M3(p * 2^8)
 
 // 16-byte chunk swizzles for E4M3 tiles (rows of D bytes): K is read 16 B per
 // lane from consecutive rows at one chunk; V is read by 16-lane groups as 8
@@ -50,208 +57,303 @@ __device__ __forceinline__ int cvt4(float a, float b, float c, float d) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2)
-void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
-                         const uint8_t* __restrict__ V, uint16_t* __restrict__ O,
-                         float* __restrict__ LSE, const float* __restrict__ DQ,
-                         const float* __restrict__ DK, const float* __restrict__ DV, int N,
-                         int nqt, float c0, int causal, int window, int qsign) {
-  constexpr int DCH = D / 16;                  // 16-byte chunks per row
-  constexpr int KSTEPS = D / 64;               // MFMA k-steps of QK^T
-  constexpr int DBLK = D / 32;                 // 32-wide d blocks of O^T
-  constexpr int TILE = kBN * D;                // bytes of one K or V tile
-  constexpr int LOADS = kBN * DCH / kThreads;  // 16-byte loads per thread per tile
-  constexpr float kPScale = 256.f;             // P is stored as E4M3(p * 2^8)
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K0 K1 V0 V1
-  lds_char* lds = (lds_char*)smem;
+struct Fp8Fwd {
+  static constexpr int BN = kBN8;
+  static constexpr int DCH = D / 16;                    // 16-byte chunks per row
+  static constexpr int KSTEPS = D / 64;                 // MFMA k-steps of QK^T
+  static constexpr int DBLK = D / 32;                   // 32-wide d blocks of O^T
+  static constexpr int NKB = BN / 32;                   // 32-key blocks of S^T
+  static constexpr int TILE = BN * D;                   // bytes of one K or V tile
+  static constexpr int LOADS = TILE / (16 * kThreads);  // 16-byte copies per thread
 
-  const TileRange tr = tile_range(N, nqt, causal, window);
-  const int bh = tr.bh, q0 = tr.q0, kt0 = tr.kt0, kt1 = tr.kt1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int qrow = q0 + wave * 32 + l32;
-  const size_t head = (size_t)bh * N * D;
-  const int nsb = (N + 127) / 128;             // scaling blocks per head
-  const float* dk = DK + (size_t)bh * nsb;
-  const float* dv = DV + (size_t)bh * nsb;
-  const float cq = c0 * DQ[(size_t)bh * nsb + q0 / 128];
-
-  // Q fragments: lane holds q8[qrow][64t + 32h .. +31].
+  lds_char* kl[2];
+  lds_char* vl[2];
+  int N, causal, window, kt0, kt1, qrow;
+  int lane, wave, h, l32;
+  i32x4 kres, vres;
+  int koff[LOADS], voff[LOADS];
+  const float* dk;
+  const float* dv;
+  float cq;
+  // state
   i32x8 qf[KSTEPS];
-#pragma unroll
-  for (int t = 0; t < KSTEPS; ++t) {
-    i32x4 x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-    if (qrow < N) {
-      const uint8_t* p = Q + head + (size_t)qrow * D + 64 * t + 32 * h;
-      x0 = *(const i32x4*)p;
-      x1 = *(const i32x4*)(p + 16);
-    }
-    x0 ^= qsign;
-    x1 ^= qsign;
-    qf[t] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-  }
-
-  i32x4 kst[LOADS], vst[LOADS];
-  auto gload = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int chunk = tid + u * kThreads;
-      const int row = chunk / DCH, col = chunk % DCH;
-      const int key = kt * kBN + row;
-      if (key < N) {
-        const size_t off = head + (size_t)key * D + col * 16;
-        kst[u] = *(const i32x4*)(K + off);
-        vst[u] = *(const i32x4*)(V + off);
-      } else {
-        kst[u] = i32x4{0, 0, 0, 0};
-        vst[u] = i32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int chunk = tid + u * kThreads;
-      const int row = chunk / DCH, col = chunk % DCH;
-      *(lds_i32x4*)(lds + buf * TILE + row * D + ((col ^ swz_k8<D>(row)) << 4)) = kst[u];
-      const int vr = v8_row(row);
-      *(lds_i32x4*)(lds + (2 + buf) * TILE + vr * D + ((col ^ swz_v8<D>(vr)) << 4)) = vst[u];
-    }
-  };
-
   f32x16 oacc[DBLK];
-#pragma unroll
-  for (int db = 0; db < DBLK; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY;                          // running max of c * s (base 2)
-  float l = 0.f;                                // running sum (this lane's keys)
-  float v_unit = kt0 < kt1 ? dv[(kt0 * kBN) / 128] : 1.f;  // descale O is kept in
+  f32x16 sacc[NKB];
+  i32x8 pbuf[2];
+  i32x8 kf[NKB][KSTEPS];
+  i32x8 vf[DBLK];
+  float m, l;
+  float alpha;        // rescale owed by O before the next PV (incl. V unit change)
+  float v_unit;       // V descale whose units O is kept in
+  bool owe_rescale;
 
-  if (kt0 < kt1) {
-    gload(kt0);
-    sstore(0);
+  template <int ST>
+  __device__ __forceinline__ void issue_k(int kt) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff[u], kt * BN * D);
   }
-  __syncthreads();
-
-  // One key tile; only EDGE tiles carry mask code.
-  auto step = [&](auto edge_tag, int kt) __attribute__((always_inline)) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
-    const int buf = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) gload(kt + 1);
-    const lds_char* Ks = lds + buf * TILE;
-    const lds_char* Vs = lds + (2 + buf) * TILE;
-    const int k0 = kt * kBN;
-    const float c = cq * dk[k0 / 128];
-    const float dv_t = dv[k0 / 128];
-
-    // ---- S^T = K Q^T (fp8 x fp8 -> fp32)
-    f32x16 sacc[2];
+  template <int ST>
+  __device__ __forceinline__ void issue_v(int kt) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int u = 0; u < LOADS; ++u)
+      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff[u], kt * BN * D);
+  }
+
+  // A operand of S^T = K Q^T: lane holds K8[32 kb + l32][64 t + 32 h .. +31].
+  template <int ST>
+  __device__ __forceinline__ void read_k() {
+    const lds_char* Ks = kl[ST];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
       const int row = kb * 32 + l32;
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
         const int ch = 4 * t + 2 * h;
         const i32x4 a0 = *(const lds_i32x4*)(Ks + row * D + ((ch ^ swz_k8<D>(row)) << 4));
         const i32x4 a1 = *(const lds_i32x4*)(Ks + row * D + (((ch + 1) ^ swz_k8<D>(row)) << 4));
-        const i32x8 kf = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[t], sacc[kb], 0, 0, 0, 0,
-                                                                   0, 0);
+        kf[kb][t] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       }
     }
+  }
+  // A operand of O^T += V^T P^T: lane (d, h) reads LDS rows 16t + 8h .. +7 of
+  // column d for t = 0..3 (the swapped key order makes these its P's keys).
+  template <int ST>
+  __device__ __forceinline__ void read_v() {
+    const lds_char* Vs = vl[ST];
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const int col = db * 32 + 16 * (g & 1) + 8 * (sl & 1);  // this source lane's 8 bytes
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 16 * t + 8 * (g >> 1) + (sl >> 1);
+        const int a = r * D + (((col >> 4) ^ swz_v8<D>(r)) << 4) + (col & 15);
+        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vs + a));
+        vf[db][2 * t] = x[0];
+        vf[db][2 * t + 1] = x[1];
+      }
+    }
+  }
 
-    // ---- online softmax (identical to the bf16 kernel, per-tile scale c)
+  __device__ __forceinline__ void qk() {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t)
+        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[kb][t], qf[t], sacc[kb], 0, 0,
+                                                                   0, 0, 0, 0);
+  }
+
+  template <int PB>
+  __device__ __forceinline__ void pv() {
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db], pbuf[PB], oacc[db], 0, 0, 0,
+                                                                 0, 0, 0);
+  }
+
+  // Online softmax of S(kt) into P set PB (E4M3 of p * 2^8; byte j of the
+  // operand is the key of sacc[j / 16][j % 16]).
+  template <bool EDGE, int PB>
+  __device__ __forceinline__ void softmax(int kt) {
+    const int k0 = kt * BN;
+    const float c = cq * dk[k0 / 128];
+    const float dv_t = dv[k0 / 128];
     if constexpr (EDGE) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
           if (!key_allowed(key, qrow, N, causal, window)) sacc[kb][i] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    float sv[16 * NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = halves_max(mx);
-    const float mnew = fmaxf(m, mx == -INFINITY ? -INFINITY : mx * c);
+      for (int i = 0; i < 16; ++i) sv[16 * kb + i] = sacc[kb][i];
+    float mx = halves_max(tree_max<16 * NKB>(sv));
+    const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
+    const float mnew = fmaxf(m, mxs);
     const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = fast_exp2(m - muse);
-
-    // P as E4M3(p * 256), byte j of the B operand = key of sacc[j / 16][j % 16]
-    i32x8 pf;
-    float rs = 0.f;
+    const float a = fast_exp2(m - muse);
+    // stored value p * 2^8 = 2^(c s - (muse - 8))
+    const float bias = muse - kPScaleLog2;
+    float ps[16 * NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float s = sacc[kb][4 * w + e];
-          p[e] = fast_exp2(fmaf(s, c, -muse));
-          if constexpr (EDGE) p[e] = s == -INFINITY ? 0.f : p[e];
-          rs += p[e];
-        }
-        pf[4 * kb + w] = cvt4(p[0] * kPScale, p[1] * kPScale, p[2] * kPScale, p[3] * kPScale);
-      }
-    l = l * alpha + rs;
-    const float f = alpha * (v_unit / dv_t);   // also moves O into dv_t units
-    if (__ballot(f != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) oacc[db] *= f;
+    for (int e = 0; e < 16 * NKB; ++e) {
+      ps[e] = fast_exp2(fmaf(sv[e], c, -bias));
+      if constexpr (EDGE) ps[e] = sv[e] == -INFINITY ? 0.f : ps[e];
     }
-    v_unit = dv_t;
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+      pbuf[PB][w] = cvt4(ps[4 * w], ps[4 * w + 1], ps[4 * w + 2], ps[4 * w + 3]);
+    // row sum of the unrounded p, as a tree, back in units of p
+    float part[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) part[w] = (ps[4 * w] + ps[4 * w + 1]) + (ps[4 * w + 2] + ps[4 * w + 3]);
+    const float rs = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+    l = l * a + rs * fast_exp2(-kPScaleLog2);
     m = mnew;
+    // O (units of v_unit) must become a * O in units of dv_t before PV(kt)
+    alpha = a * (v_unit / dv_t);
+    v_unit = dv_t;
+    owe_rescale = __ballot(alpha != 1.f) != 0;
+  }
 
-    // ---- O^T += V^T P^T: one K=64 MFMA per 32-wide d block. Lane (d, h)
-    //      reads LDS rows 16t + 8h .. +7 of column d for t = 0..3.
-    const int g = lane >> 4, sl = lane & 15;
+  __device__ __forceinline__ void rescale() {
+    if (owe_rescale) {
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const int col = db * 32 + 16 * (g & 1) + 8 * (sl & 1);   // this source lane's 8 bytes
-      i32x8 va;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 16 * t + 8 * (g >> 1) + (sl >> 1);
-        const int a = r * D + (((col >> 4) ^ swz_v8<D>(r)) << 4) + (col & 15);
-        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vs + a));
-        va[2 * t] = x[0];
-        va[2 * t + 1] = x[1];
-      }
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf, oacc[db], 0, 0, 0, 0, 0, 0);
+      for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
     }
+  }
 
-    if (more) sstore(buf ^ 1);
-    __syncthreads();
-  };
+  __device__ __forceinline__ void sync_tiles() {
+    wait_vmem();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  }
 
-  const InteriorSpan span = interior_span(tr, N, causal, window);
-  int kt = kt0;
-  for (; kt < span.ia; ++kt) step(std::true_type{}, kt);
-  for (; kt < span.ib; ++kt) step(std::false_type{}, kt);
-  for (; kt < kt1; ++kt) step(std::true_type{}, kt);
+  template <bool EDGE, int PB, bool FIRST>
+  __device__ __forceinline__ void iteration(int j) {
+    sync_tiles();                           // K_j, V_{j-1} landed; iteration j-1 done
+    issue_k<PB ^ 1>(j + 1);                 // unconditional: see the bf16 kernel
+    issue_v<PB>(j);
+    read_k<PB>();
+    if constexpr (!FIRST) read_v<PB ^ 1>();
+    qk();
+    rescale();
+    if constexpr (!FIRST) pv<PB ^ 1>();
+    softmax<EDGE, PB>(j);
+    __builtin_amdgcn_iglp_opt(0);
+  }
 
-  // ---- epilogue: O = O_acc * dv_last / (256 l), LSE = ln 2 * (m + log2 l)
-  const float lt = halves_sum(l);
-  const float inv = lt > 0.f ? v_unit / (kPScale * lt) : 0.f;
-  if (qrow < N) {
-    uint16_t* orow = O + head + (size_t)qrow * D;
+  template <bool EDGE>
+  __device__ __forceinline__ void run(int j0, int j1) {
+    int j = j0;
+    if (j < j1 && ((j - kt0) & 1)) iteration<EDGE, 1, false>(j++);
+    for (; j + 1 < j1; j += 2) {
+      iteration<EDGE, 0, false>(j);
+      iteration<EDGE, 1, false>(j + 1);
+    }
+    if (j < j1) iteration<EDGE, 0, false>(j);
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2)
+void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
+                         const uint8_t* __restrict__ V, uint16_t* __restrict__ O,
+                         float* __restrict__ LSE, const float* __restrict__ DQ,
+                         const float* __restrict__ DK, const float* __restrict__ DV, int N,
+                         int nqt, float c0, int causal, int window, int qsign) {
+  using S = Fp8Fwd<D>;
+  __shared__ __attribute__((aligned(1024))) char k0s[S::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[S::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[S::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[S::TILE];
+
+  S st;
+  st.kl[0] = (lds_char*)k0s;
+  st.kl[1] = (lds_char*)k1s;
+  st.vl[0] = (lds_char*)v0s;
+  st.vl[1] = (lds_char*)v1s;
+  const TileRange tr = tile_range(N, nqt, causal, window, kBM, S::BN);
+  st.N = N;
+  st.causal = causal;
+  st.window = window;
+  st.kt0 = tr.kt0;
+  st.kt1 = tr.kt1;
+  const int tid = threadIdx.x;
+  st.lane = tid & 63;
+  st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  st.h = st.lane >> 5;
+  st.l32 = st.lane & 31;
+  st.qrow = tr.q0 + st.wave * 32 + st.l32;
+  const size_t head = (size_t)tr.bh * N * D;
+  const int nsb = (N + 127) / 128;             // scaling blocks per head
+  st.dk = DK + (size_t)tr.bh * nsb;
+  st.dv = DV + (size_t)tr.bh * nsb;
+  st.cq = c0 * DQ[(size_t)tr.bh * nsb + tr.q0 / 128];
+
+  // Q fragments: lane holds q8[qrow][64t + 32h .. +31].
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
+  for (int t = 0; t < S::KSTEPS; ++t) {
+    i32x4 x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
+    if (st.qrow < N) {
+      const uint8_t* p = Q + head + (size_t)st.qrow * D + 64 * t + 32 * st.h;
+      x0 = *(const i32x4*)p;
+      x1 = *(const i32x4*)(p + 16);
+    }
+    x0 ^= qsign;
+    x1 ^= qsign;
+    st.qf[t] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  }
+
+  // HBM -> LDS copies: LDS chunk p (p = 64 * block + lane) of the K image is
+  // row p / DCH, physical column p % DCH, holding logical column
+  // (p % DCH) ^ swizzle(row). The V image's LDS row r holds key v8_row(r).
+  st.kres = make_rsrc(K + head, (uint32_t)N * D);
+  st.vres = make_rsrc(V + head, (uint32_t)N * D);
+#pragma unroll
+  for (int u = 0; u < S::LOADS; ++u) {
+    const int p = (u * 4 + st.wave) * 64 + st.lane;
+    const int row = p / S::DCH, pc = p % S::DCH;
+    st.koff[u] = row * D + (pc ^ swz_k8<D>(row)) * 16;
+    st.voff[u] = v8_row(row) * D + (pc ^ swz_v8<D>(row)) * 16;
+  }
+
+#pragma unroll
+  for (int db = 0; db < S::DBLK; ++db) st.oacc[db] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.alpha = 1.f;
+  st.owe_rescale = false;
+
+  const int kt0 = tr.kt0, kt1 = tr.kt1;
+  st.v_unit = kt0 < kt1 ? st.dv[kt0 * S::BN / 128] : 1.f;
+
+  if (kt0 < kt1) {
+    st.template issue_k<0>(kt0);
+    const InteriorSpan span = interior_span(tr, N, causal, window, S::BN);
+    if (kt0 < span.ia || kt0 >= span.ib) st.template iteration<true, 0, true>(kt0);
+    else st.template iteration<false, 0, true>(kt0);
+    const int a = min(max(span.ia, kt0 + 1), kt1), b = min(max(span.ib, a), kt1);
+    st.template run<true>(kt0 + 1, a);
+    st.template run<false>(a, b);
+    st.template run<true>(b, kt1);
+    st.sync_tiles();
+    st.rescale();
+    if ((kt1 - 1 - kt0) & 1) {
+      st.template read_v<1>();
+      st.template pv<1>();
+    } else {
+      st.template read_v<0>();
+      st.template pv<0>();
+    }
+  }
+
+  // ---- epilogue: O = O_acc * dv_last / (2^8 l), LSE = ln 2 * (m + log2 l)
+  const float lt = halves_sum(st.l);
+  const float inv = lt > 0.f ? st.v_unit * fast_exp2(-kPScaleLog2) / lt : 0.f;
+  if (st.qrow < N) {
+    uint16_t* orow = O + head + (size_t)st.qrow * D;
+#pragma unroll
+    for (int db = 0; db < S::DBLK; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         bf16x4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[db][4 * g4 + e] * inv);
-        *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * h) = o4;
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(st.oacc[db][4 * g4 + e] * inv);
+        *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * st.h) = o4;
       }
-    if (h == 0) {
-      const float muse = m == -INFINITY ? 0.f : m;
-      LSE[(size_t)bh * N + qrow] = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
+    if (st.h == 0) {
+      const float muse = st.m == -INFINITY ? 0.f : st.m;
+      LSE[(size_t)tr.bh * N + st.qrow] = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
     }
   }
 }
