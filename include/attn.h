@@ -57,7 +57,10 @@ enum {
 };
 
 /* Largest supported sizes (index arithmetic is 64-bit; these bound the grid). */
-#define ATTN_MAX_N (1 << 24)
+/* Longest sequence: one head's K or V plus a tile past its end must stay
+ * inside the 32-bit byte range of the buffer descriptors the kernels read
+ * through ((2^23 + 64) * 128 * 2 < 2^32). */
+#define ATTN_MAX_N (1 << 23)
 #define ATTN_MAX_BH (1 << 24)
 /* Rows per fp8 scaling block, for Q, K and V alike. */
 #define ATTN_FP8_BLOCK_ROWS 128

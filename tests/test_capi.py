@@ -72,7 +72,7 @@ E = header_codes()
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=-1), "ATTN_E_SHAPE"), (dict(H=-2), "ATTN_E_SHAPE"), (dict(N=-5), "ATTN_E_SHAPE"),
-    (dict(N=(1 << 24) + 1), "ATTN_E_SHAPE"), (dict(B=1 << 13, H=1 << 12), "ATTN_E_SHAPE"),
+    (dict(N=(1 << 23) + 1), "ATTN_E_SHAPE"), (dict(B=1 << 13, H=1 << 12), "ATTN_E_SHAPE"),
     (dict(d=96), "ATTN_E_HEADDIM"), (dict(d=256), "ATTN_E_HEADDIM"), (dict(d=0), "ATTN_E_HEADDIM"),
     (dict(dtype=2), "ATTN_E_DTYPE"), (dict(dtype=-1), "ATTN_E_DTYPE"),
     (dict(q=None), "ATTN_E_NULL"), (dict(k=None), "ATTN_E_NULL"), (dict(v=None), "ATTN_E_NULL"),
@@ -110,7 +110,7 @@ def call_quant(lib, x=A, x8=A + GAP, ds=A + 2 * GAP, B=2, H=3, N=300, d=128, per
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(B=-1), "ATTN_E_SHAPE"), (dict(N=(1 << 24) + 1), "ATTN_E_SHAPE"),
+    (dict(B=-1), "ATTN_E_SHAPE"), (dict(N=(1 << 23) + 1), "ATTN_E_SHAPE"),
     (dict(d=32), "ATTN_E_HEADDIM"),
     (dict(x=None), "ATTN_E_NULL"), (dict(x8=None), "ATTN_E_NULL"), (dict(ds=None), "ATTN_E_NULL"),
     (dict(per_tensor=2), "ATTN_E_DTYPE"),

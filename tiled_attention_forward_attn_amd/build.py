@@ -35,13 +35,27 @@ COMMON_FLAGS = [
 ]
 
 
+# The attention kernels assume NaN-free scores: without this, every two-input
+# max of MFMA results gets two extra instructions that quiet signalling NaNs
+# (infinities keep their meaning; masked scores are -inf). Inputs holding NaN
+# give undefined outputs either way.
+FILE_FLAGS = {
+    "attn_fwd_bf16.hip": ["-fno-honor-nans"],
+    "attn_fwd_fp8.hip": ["-fno-honor-nans"],
+}
+
+
+def flags_for(src: str) -> list[str]:
+    return COMMON_FLAGS + FILE_FLAGS.get(os.path.basename(src), [])
+
+
 def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *flags_for(src), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -73,27 +73,42 @@ __device__ __forceinline__ int xcd_remap(int w, int G) {
   return x * q + min(x, r) + slot;
 }
 
+// max(a, b) as v_med3_f32(a, b, +inf). A two-input fmaxf makes the compiler
+// quiet both inputs first (two extra v_max_f32 x, x, x when they come from
+// an MFMA or a lane permute); the three-input forms need no such step.
+__device__ __forceinline__ float max2(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, INFINITY);
+}
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
 // v_permlane32_swap of a value with itself leaves, in every lane l, the pair
 // {x[l % 32], x[l % 32 + 32]} (in some order): the two halves of one query row
 // in the S^T accumulator layout.
 __device__ __forceinline__ float halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halves_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Max of an array as a tree of v_max3_f32 (short dependency chains).
+// Max of an array as levels of v_max3_f32 (N - 1 comparisons in about
+// (N - 1) / 2 instructions, short dependency chains).
 template <int N>
 __device__ __forceinline__ float tree_max(const float* x) {
-  if constexpr (N == 1) return x[0];
-  else if constexpr (N == 2) return fmaxf(x[0], x[1]);
-  else if constexpr (N == 3) return fmaxf(fmaxf(x[0], x[1]), x[2]);
-  else {
-    constexpr int T = N / 3;
-    return fmaxf(fmaxf(tree_max<T>(x), tree_max<T>(x + T)), tree_max<N - 2 * T>(x + 2 * T));
+  if constexpr (N == 1) {
+    return x[0];
+  } else if constexpr (N == 2) {
+    return max2(x[0], x[1]);
+  } else {
+    constexpr int G = N / 3, R = N % 3, M = G + (R == 1 ? 1 : 0);
+    float y[M];
+#pragma unroll
+    for (int i = 0; i < G; ++i) y[i] = max3(x[3 * i], x[3 * i + 1], x[3 * i + 2]);
+    if constexpr (R == 2) y[G - 1] = max3(x[N - 2], x[N - 1], y[G - 1]);
+    if constexpr (R == 1) y[G] = x[N - 1];
+    return tree_max<M>(y);
   }
 }
 

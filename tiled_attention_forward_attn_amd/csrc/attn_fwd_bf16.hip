@@ -29,9 +29,12 @@
 //    interleaved with the softmax of S(j), so the exponentials run while the
 //    matrix cores are busy. P alternates between two register sets.
 //  * Online softmax in base 2 with log2(e) folded into the scale (v_exp_f32
-//    computes 2^x). A row's reference max only moves when its max exceeds it
-//    by more than 8, so p <= 2^8 and the O rescale (owed to the next
-//    iteration, before its PV) is rare; O / l and the LSE are unchanged.
+//    computes 2^x). A tile is first exponentiated against the row's current
+//    reference max; only if some lane's sum of p exceeds a bound (first tile,
+//    scores far above the reference, Inf/NaN) does the wave compute the row
+//    max, move the reference (when the max exceeds it by more than 8) and
+//    redo the tile. So the row max and the O rescale (owed to the next
+//    iteration, before its PV) are rare; O / l and the LSE are unchanged.
 //  * Key tiles wholly outside the causal / sliding-window band are never
 //    visited ([YT] section 2.1.2); only tiles straddling the band's edge or the
 //    ragged end of the sequence carry mask code.
@@ -75,6 +78,10 @@ struct Bf16Fwd {
   static constexpr int PST = BN / 16;                   // 16-key MFMA steps of PV
   static constexpr int TILE = BN * D * 2;               // bytes of one K or V tile
   static constexpr int LOADS = TILE / (16 * kThreads);  // 16-byte copies per thread
+  // Largest accepted sum of one lane's p without a new reference max: with
+  // the exact step's slack every p <= 2^8, so this is never exceeded
+  // right after it; it bounds every p by 16 NKB 2^8.
+  static constexpr float kFastLimit = 16.f * NKB * 256.f;
 
   // problem
   lds_char* kl[2];   // K stages: K_t lives in stage (t - kt0) & 1
@@ -99,13 +106,13 @@ struct Bf16Fwd {
   __device__ __forceinline__ void issue_k(int kt) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
-      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff[u], kt * BN * D * 2);
+      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff[u], (int)((uint32_t)kt * (BN * D * 2)));
   }
   template <int ST>
   __device__ __forceinline__ void issue_v(int kt) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
-      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff[u], kt * BN * D * 2);
+      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff[u], (int)((uint32_t)kt * (BN * D * 2)));
   }
 
   // A operand of S^T = K Q^T: lane holds K[32 kb + l32][16 t + 8 h .. +7].
@@ -170,50 +177,83 @@ struct Bf16Fwd {
           oacc[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s][db], pbuf[PB][b][s], oacc[b][db], 0, 0, 0);
   }
 
-  // Online softmax of S(kt) into P set PB. sacc[b][kb][i] is the score of key
-  // k0 + 32 kb + 8 (i/4) + 4 h + i%4 against query qrow[b].
-  template <bool EDGE, int PB>
-  __device__ __forceinline__ void softmax(int kt) {
+  // Disallowed keys of an edge tile get score -inf. sacc[b][kb][i] is the
+  // score of key k0 + 32 kb + 8 (i/4) + 4 h + i%4 against query qrow[b].
+  __device__ __forceinline__ void mask(int kt) {
     const int k0 = kt * BN;
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (!key_allowed(key, qrow[b], N, causal, window)) sacc[b][kb][i] = -INFINITY;
+        }
+  }
+
+  // P set PB of query block b = bf16(2^(c s - muse)) (masked keys 0); returns
+  // this lane's sum of the rounded values (the ones PV multiplies).
+  template <bool EDGE, int PB>
+  __device__ __forceinline__ float exponentiate(int b, float muse) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(sacc[b][kb][i], c, -muse));
+        if constexpr (EDGE) p = sacc[b][kb][i] == -INFINITY ? 0.f : p;
+        pbuf[PB][b][kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
+      }
+    float part[PST];
+#pragma unroll
+    for (int st = 0; st < PST; ++st) part[st] = sum_bf16x8(pbuf[PB][b][st], 0.f);
+    float rs = part[0];
+#pragma unroll
+    for (int st = 1; st < PST; ++st) rs += part[st];
+    return rs;
+  }
+
+  // Online softmax of S(kt) into P set PB.
+  //
+  // Common case: exponentiate against the current reference max m and accept
+  // the tile if every lane's sum of its p stays <= kFastLimit (so each p is
+  // bounded, and O, l need no rescale). No row max is computed.
+  // Otherwise (first tile, a score far above m, Inf or NaN), the whole wave
+  // takes the exact step: row max over both half-rows, m moves to it when it
+  // exceeds m by more than kRescaleSlack, O's rescale is owed, P recomputed.
+  template <bool EDGE, int PB, bool FIRST>
+  __device__ __forceinline__ void softmax(int kt) {
+    if constexpr (EDGE) mask(kt);
+    if constexpr (!FIRST) {
+      float rs[QB];
+      bool over = false;
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        rs[b] = exponentiate<EDGE, PB>(b, m[b]);
+        over = over || !(rs[b] <= kFastLimit);
+      }
+      if (__ballot(over) == 0) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) l[b] += rs[b];
+        owe_rescale = false;
+        return;
+      }
+    }
     bool grow_any = false;
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
-      if constexpr (EDGE) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (!key_allowed(key, qrow[b], N, causal, window)) sacc[b][kb][i] = -INFINITY;
-          }
-      }
       float sv[16 * NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sv[16 * kb + i] = sacc[b][kb][i];
-      float mx = tree_max<16 * NKB>(sv);
-      mx = halves_max(mx);
+      const float mx = halves_max(tree_max<16 * NKB>(sv));
       const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
       const bool grow = mxs > m[b] + kRescaleSlack;
       const float mnew = grow ? mxs : m[b];
       const float muse = mnew == -INFINITY ? 0.f : mnew;
       const float a = fast_exp2(m[b] - muse);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(fmaf(sacc[b][kb][i], c, -muse));
-          if constexpr (EDGE) p = sacc[b][kb][i] == -INFINITY ? 0.f : p;
-          pbuf[PB][b][kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
-        }
-      // row sum of the rounded P (the values PV multiplies), 2 per v_dot2
-      float part[PST];
-#pragma unroll
-      for (int st = 0; st < PST; ++st) part[st] = sum_bf16x8(pbuf[PB][b][st], 0.f);
-      float rs = part[0];
-#pragma unroll
-      for (int st = 1; st < PST; ++st) rs += part[st];
+      const float rs = exponentiate<EDGE, PB>(b, muse);
       l[b] = l[b] * a + rs;
       alpha[b] = a;
       m[b] = mnew;
@@ -259,7 +299,7 @@ struct Bf16Fwd {
     qk();
     rescale();
     if constexpr (!FIRST) pv<PB ^ 1>();
-    softmax<EDGE, PB>(j);
+    softmax<EDGE, PB, FIRST>(j);
     __builtin_amdgcn_iglp_opt(0);
   }
 

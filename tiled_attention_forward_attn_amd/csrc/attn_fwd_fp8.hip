@@ -91,13 +91,13 @@ struct Fp8Fwd {
   __device__ __forceinline__ void issue_k(int kt) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
-      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff[u], kt * BN * D);
+      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff[u], (int)((uint32_t)kt * (BN * D)));
   }
   template <int ST>
   __device__ __forceinline__ void issue_v(int kt) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
-      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff[u], kt * BN * D);
+      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff[u], (int)((uint32_t)kt * (BN * D)));
   }
 
   // A operand of S^T = K Q^T: lane holds K8[32 kb + l32][64 t + 32 h .. +31].
@@ -178,7 +178,7 @@ struct Fp8Fwd {
       for (int i = 0; i < 16; ++i) sv[16 * kb + i] = sacc[kb][i];
     float mx = halves_max(tree_max<16 * NKB>(sv));
     const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
-    const float mnew = fmaxf(m, mxs);
+    const float mnew = max2(m, mxs);
     const float muse = mnew == -INFINITY ? 0.f : mnew;
     const float a = fast_exp2(m - muse);
     // stored value p * 2^8 = 2^(c s - (muse - 8))
@@ -199,8 +199,10 @@ struct Fp8Fwd {
     const float rs = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
     l = l * a + rs * fast_exp2(-kPScaleLog2);
     m = mnew;
-    // O (units of v_unit) must become a * O in units of dv_t before PV(kt)
-    alpha = a * (v_unit / dv_t);
+    // O (units of v_unit) must become a * O in units of dv_t before PV(kt);
+    // the unit ratio is exactly 1 inside one V block (v_rcp_f32: 1 ulp)
+    const float ratio = dv_t == v_unit ? 1.f : v_unit * __builtin_amdgcn_rcpf(dv_t);
+    alpha = a * ratio;
     v_unit = dv_t;
     owe_rescale = __ballot(alpha != 1.f) != 0;
   }
