@@ -39,7 +39,9 @@ extern "C" {
 /* Element type of q, k, v for attn_fwd. o is always bf16, lse always fp32. */
 typedef enum {
   ATTN_DTYPE_BF16 = 0,      /* q, k, v bf16; bf16 MFMA contractions                 */
-  ATTN_DTYPE_FP8_E4M3 = 1   /* q, k, v E4M3 codes with per-block descales; fp8 MFMA */
+  ATTN_DTYPE_FP8_E4M3 = 1,  /* q, k, v E4M3 codes with per-block descales; fp8 MFMA */
+  ATTN_DTYPE_FP8_PV = 2     /* q, k bf16 (S = Q K^T on bf16 MFMAs); v E4M3 codes with
+                               per-block descales, P in E4M3, O += P V on fp8 MFMAs  */
 } attn_dtype;
 
 /* Return codes. */
@@ -70,14 +72,15 @@ enum {
  *
  * Computes, for every batch b, head h and query row i, over the allowed key
  * set A(i):
- *   s_ij = scale * <q_i, k_j>  (fp8: scale * dq * dk * <q8_i, k8_j>)
- *   o_i  = sum_{j in A(i)} softmax_j(s_i) * v_j    (fp8: v_j = v8_j * dv)
+ *   s_ij = scale * <q_i, k_j>  (dtype 1: scale * dq * dk * <q8_i, k8_j>)
+ *   o_i  = sum_{j in A(i)} softmax_j(s_i) * v_j    (dtypes 1, 2: v_j = v8_j * dv)
  *   lse_i = ln sum_{j in A(i)} exp(s_ij)           (natural log)
  * The tiled, online-softmax evaluation follows [WGC] section 2 (local max and
  * sum per key block, running statistics, rescale of the output) and [JJ]
  * section 2.4; the fused softmax + mask + matmul follows [YT] section 1.2.
  *
- *   q, k, v   [B][H][N][d], bf16 (dtype 0) or E4M3 bytes (dtype 1). Read only.
+ *   q, k, v   [B][H][N][d]. Read only. dtype 0: all bf16; dtype 1: all E4M3
+ *             bytes; dtype 2: q and k bf16, v E4M3 bytes.
  *   o         [B][H][N][d] bf16 output (fp32 accumulation, rounded to nearest
  *             even at the end: [WGC] section 3).
  *   lse       [B][H][N] fp32 output, may NOT be NULL.
@@ -92,12 +95,17 @@ enum {
  *             values are allowed.
  *   dtype     attn_dtype.
  *   descale_q, descale_k, descale_v
- *             fp8 only (ignored and may be NULL for bf16): fp32
- *             [B][H][ceil(N/128)] dequantisation factors, one per 128-row block
- *             of the corresponding tensor, as written by attn_fp8_quantize
- *             ([WGC] section 3, per-block scaling).
+ *             fp32 [B][H][ceil(N/128)] dequantisation factors, one per 128-row
+ *             block of the corresponding E4M3 tensor, as written by
+ *             attn_fp8_quantize ([WGC] section 3, per-block scaling). dtype 1
+ *             needs all three; dtype 2 needs descale_v only; the others are
+ *             ignored and may be NULL.
  *   stream    hipStream_t or NULL.
  *
+ * dtype 2 keeps the score contraction in bf16 and only P and V in E4M3 (the
+ * FP8 GEMM of [JJ] section 2.3 for PV alone): on data whose large outlier
+ * channels are shared by Q and K, E4M3 scores carry an error that grows with
+ * |s|, and this mode removes it at the cost of bf16 speed for QK^T.
  * A row whose allowed set is empty (impossible with the masks above, since
  * j = i is always allowed) would get o = 0 and lse = -inf.
  * Returns ATTN_OK or an ATTN_E_* code.

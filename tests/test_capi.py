@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strerror(lib):
-    assert tafa.version() == 10000
+    assert tafa.version() == 10100
     codes = header_codes()
     assert codes["ATTN_OK"] == 0
     texts = {tafa.strerror(c) for c in codes.values()}
@@ -74,7 +74,7 @@ E = header_codes()
     (dict(B=-1), "ATTN_E_SHAPE"), (dict(H=-2), "ATTN_E_SHAPE"), (dict(N=-5), "ATTN_E_SHAPE"),
     (dict(N=(1 << 23) + 1), "ATTN_E_SHAPE"), (dict(B=1 << 13, H=1 << 12), "ATTN_E_SHAPE"),
     (dict(d=96), "ATTN_E_HEADDIM"), (dict(d=256), "ATTN_E_HEADDIM"), (dict(d=0), "ATTN_E_HEADDIM"),
-    (dict(dtype=2), "ATTN_E_DTYPE"), (dict(dtype=-1), "ATTN_E_DTYPE"),
+    (dict(dtype=3), "ATTN_E_DTYPE"), (dict(dtype=-1), "ATTN_E_DTYPE"),
     (dict(q=None), "ATTN_E_NULL"), (dict(k=None), "ATTN_E_NULL"), (dict(v=None), "ATTN_E_NULL"),
     (dict(o=None), "ATTN_E_NULL"), (dict(lse=None), "ATTN_E_NULL"),
     (dict(dtype=1), "ATTN_E_NULL"),
@@ -88,6 +88,11 @@ E = header_codes()
     (dict(o=A), "ATTN_E_ALIAS"), (dict(o=A + GAP + 1024), "ATTN_E_ALIAS"),
     (dict(lse=A + 2 * GAP + 64), "ATTN_E_ALIAS"), (dict(lse=A + 3 * GAP + 16), "ATTN_E_ALIAS"),
     (dict(dtype=1, dq=A + 3 * GAP, dk=A + 6 * GAP, dv=A + 7 * GAP), "ATTN_E_ALIAS"),
+    # dtype 2 (q, k bf16; v E4M3): only descale_v is required
+    (dict(dtype=2), "ATTN_E_NULL"), (dict(dtype=2, dq=A + 5 * GAP, dk=A + 6 * GAP), "ATTN_E_NULL"),
+    (dict(dtype=2, dv=A + 7 * GAP + 2), "ATTN_E_ALIGN"),
+    (dict(dtype=2, dv=A + 3 * GAP + 64), "ATTN_E_ALIAS"),
+    (dict(dtype=2, dv=A + 7 * GAP, o=A + 2 * GAP + 1024), "ATTN_E_ALIAS"),
 ])
 def test_attn_fwd_rejects(lib, kw, code):
     assert call_fwd(lib, **kw) == E[code]
@@ -98,11 +103,29 @@ def test_attn_fwd_empty_problem_is_ok(lib):
         assert call_fwd(lib, **kw) == E["ATTN_OK"]
 
 
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+# These calls pass validation with fake addresses and reach the launch, which
+# fails cleanly only where there is no GPU.
+@pytest.mark.skipif(not _no_gpu(), reason="fake device addresses would reach a real kernel")
 def test_attn_fwd_output_right_after_input_is_not_alias(lib):
     # q occupies [A, A + 2*3*300*128*2); o starting right after it is legal
     qbytes = 2 * 3 * 300 * 128 * 2
     rc = call_fwd(lib, o=A + qbytes + (16 - qbytes % 16) % 16)
     assert rc != E["ATTN_E_ALIAS"]
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake device addresses would reach a real kernel")
+def test_fp8_pv_checks_v_at_one_byte_per_element(lib):
+    # dtype 2's v holds 1 byte per element: o right after that extent is legal,
+    # while the same placement overlaps a bf16 v
+    vbytes = 2 * 3 * 300 * 128
+    o = A + 2 * GAP + vbytes
+    assert call_fwd(lib, dtype=2, dv=A + 7 * GAP, o=o) != E["ATTN_E_ALIAS"]
+    assert call_fwd(lib, dtype=0, o=o) == E["ATTN_E_ALIAS"]
 
 
 def call_quant(lib, x=A, x8=A + GAP, ds=A + 2 * GAP, B=2, H=3, N=300, d=128, per_tensor=0):

@@ -25,6 +25,7 @@ BLOCK_ROWS = 128                      # rows per fp8 scaling block
 
 DTYPE_BF16 = 0
 DTYPE_FP8_E4M3 = 1
+DTYPE_FP8_PV = 2
 
 _lib: ctypes.CDLL | None = None
 _vp = ctypes.c_void_p
@@ -94,29 +95,42 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
     """Attention forward through attn_fwd. Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N]).
 
-    q, k, v: bf16, or E4M3 codes (uint8 / float8_e4m3fn) with
-    descales=(dq, dk, dv) fp32 [B, H, ceil(N/128)]. scale=None means 1/sqrt(d).
+    q, k, v all bf16 (dtype 0); all E4M3 codes (uint8 / float8_e4m3fn) with
+    descales=(dq, dk, dv) fp32 [B, H, ceil(N/128)] (dtype 1); or q, k bf16 and
+    v E4M3 codes with descales=(None, None, dv) (dtype 2: scores in bf16, P
+    and V in E4M3). scale=None means 1/sqrt(d).
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_4d(name, t)
     if not (q.shape == k.shape == v.shape):
         raise ValueError("q, k and v must have the same shape")
     B, H, N, d = q.shape
-    fp8 = _is_fp8(q)
-    if fp8 != _is_fp8(k) or fp8 != _is_fp8(v) or (not fp8 and not (q.dtype == k.dtype == v.dtype == torch.bfloat16)):
-        raise ValueError("q, k, v must all be bf16 or all be E4M3 codes")
-    if fp8 and descales is None:
-        raise ValueError("fp8 inputs need descales=(dq, dk, dv)")
+    q8, k8, v8 = _is_fp8(q), _is_fp8(k), _is_fp8(v)
+    bf = [t.dtype == torch.bfloat16 for t in (q, k, v)]
+    if q8 and k8 and v8:
+        dtype = DTYPE_FP8_E4M3
+    elif bf[0] and bf[1] and v8:
+        dtype = DTYPE_FP8_PV
+    elif all(bf):
+        dtype = DTYPE_BF16
+    else:
+        raise ValueError("q, k, v must be all bf16, all E4M3 codes, or bf16 q, k with E4M3 v")
+    if dtype != DTYPE_BF16:
+        if descales is None or len(descales) != 3 or descales[2] is None:
+            raise ValueError("E4M3 inputs need descales=(dq, dk, dv) (dq, dk None when q, k are bf16)")
+        if dtype == DTYPE_FP8_E4M3 and (descales[0] is None or descales[1] is None):
+            raise ValueError("all-E4M3 inputs need dq and dk")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    dq, dk, dv = descales if fp8 else (None, None, None)
+    dq, dk, dv = descales if dtype != DTYPE_BF16 else (None, None, None)
+    if dtype == DTYPE_FP8_PV:
+        dq = dk = None
     rc = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
-                         int(causal), int(window), float(scale),
-                         DTYPE_FP8_E4M3 if fp8 else DTYPE_BF16,
+                         int(causal), int(window), float(scale), dtype,
                          _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream))
     if rc != 0:
         raise AttnError(rc, "attn_fwd")
@@ -142,4 +156,4 @@ def quantize(x: torch.Tensor, per_tensor: bool = False, out: torch.Tensor | None
 
 
 __all__ = ["fwd", "quantize", "load", "strerror", "version", "AttnError", "LIB_PATH",
-           "SIGNATURES", "BLOCK_ROWS", "DTYPE_BF16", "DTYPE_FP8_E4M3"]
+           "SIGNATURES", "BLOCK_ROWS", "DTYPE_BF16", "DTYPE_FP8_E4M3", "DTYPE_FP8_PV"]

@@ -21,9 +21,16 @@
 //    last one. (Folding dv_t / u into P instead would save that rescale but
 //    round the largest weight: measured 6x the kernel error on outlier data
 //    for a 4.5% speed gain.)
+// A second instance (QBF) keeps Q and K in bf16 and computes S = Q K^T on the
+// bf16 matrix cores, with only V and P in E4M3: the score error that E4M3 Q
+// and K carry on data with large, aligned outlier channels (it grows with
+// |s|) is gone, while PV keeps the fp8 contraction. Everything from the
+// scores on is shared with the all-E4M3 instance.
 // The V tile is stored in LDS with bits 2 and 3 of each key offset swapped, so
 // that ds_read_b64_tr_b8 (8 consecutive LDS rows of one column per lane) hands
 // every lane exactly the 32 keys whose probabilities it holds in registers.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -46,6 +53,13 @@ __device__ __forceinline__ int swz_v8(int r) {
   if constexpr (D == 128) return r & 7;
   else return (r >> 1) & 3;
 }
+// 16-byte chunk swizzle of a bf16 K tile (rows of 2 D bytes), read 16 B per
+// lane from 32 consecutive rows at one chunk column.
+template <int D>
+__device__ __forceinline__ int swz_k16(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return ((r >> 1) & 7) ^ ((r & 1) << 2);
+}
 // LDS row of key offset k within a tile: swap bits 2 and 3 (an involution).
 __device__ __forceinline__ int v8_row(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
@@ -56,31 +70,37 @@ __device__ __forceinline__ int cvt4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-template <int D>
+// QBF: Q and K are bf16 and S = Q K^T runs on bf16 MFMAs; otherwise all E4M3.
+template <int D, bool QBF>
 struct Fp8Fwd {
+  using QKFrag = std::conditional_t<QBF, bf16x8, i32x8>;
   static constexpr int BN = kBN8;
-  static constexpr int DCH = D / 16;                    // 16-byte chunks per row
-  static constexpr int KSTEPS = D / 64;                 // MFMA k-steps of QK^T
-  static constexpr int DBLK = D / 32;                   // 32-wide d blocks of O^T
-  static constexpr int NKB = BN / 32;                   // 32-key blocks of S^T
-  static constexpr int TILE = BN * D;                   // bytes of one K or V tile
-  static constexpr int LOADS = TILE / (16 * kThreads);  // 16-byte copies per thread
+  static constexpr int KSTEPS = QBF ? D / 16 : D / 64;      // MFMA k-steps of QK^T
+  static constexpr int DBLK = D / 32;                       // 32-wide d blocks of O^T
+  static constexpr int NKB = BN / 32;                       // 32-key blocks of S^T
+  static constexpr int KBYTES = QBF ? 2 : 1;                // bytes per Q / K element
+  static constexpr int KDCH = D * KBYTES / 16;              // 16-byte chunks per K row
+  static constexpr int VDCH = D / 16;                       // 16-byte chunks per V row
+  static constexpr int KTILE = BN * D * KBYTES;             // bytes of one K tile
+  static constexpr int VTILE = BN * D;                      // bytes of one V tile
+  static constexpr int KLOADS = KTILE / (16 * kThreads);    // 16-byte copies per thread
+  static constexpr int VLOADS = VTILE / (16 * kThreads);
 
   lds_char* kl[2];
   lds_char* vl[2];
   int N, causal, window, kt0, kt1, qrow;
   int lane, wave, h, l32;
   i32x4 kres, vres;
-  int koff[LOADS], voff[LOADS];
+  int koff[KLOADS], voff[VLOADS];
   const float* dk;
   const float* dv;
   float cq;
   // state
-  i32x8 qf[KSTEPS];
+  QKFrag qf[KSTEPS];
   f32x16 oacc[DBLK];
   f32x16 sacc[NKB];
   i32x8 pbuf[2];
-  i32x8 kf[NKB][KSTEPS];
+  QKFrag kf[NKB][KSTEPS];
   i32x8 vf[DBLK];
   float m, l;
   float alpha;        // rescale owed by O before the next PV (incl. V unit change)
@@ -90,25 +110,28 @@ struct Fp8Fwd {
   template <int ST>
   __device__ __forceinline__ void issue_k(int kt) {
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u)
-      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff[u], (int)((uint32_t)kt * (BN * D)));
+    for (int u = 0; u < KLOADS; ++u)
+      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff[u], (int)((uint32_t)kt * KTILE));
   }
   template <int ST>
   __device__ __forceinline__ void issue_v(int kt) {
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u)
-      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff[u], (int)((uint32_t)kt * (BN * D)));
+    for (int u = 0; u < VLOADS; ++u)
+      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff[u], (int)((uint32_t)kt * VTILE));
   }
 
-  // A operand of S^T = K Q^T: lane holds K8[32 kb + l32][64 t + 32 h .. +31].
+  // A operand of S^T = K Q^T for 32-key block kb. E4M3: lane holds
+  // K8[32 kb + l32][64 t + 32 h .. +31]; bf16: K[32 kb + l32][16 t + 8 h .. +7].
   template <int ST>
-  __device__ __forceinline__ void read_k() {
+  __device__ __forceinline__ void read_k(int kb) {
     const lds_char* Ks = kl[ST];
+    const int row = kb * 32 + l32;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const int row = kb * 32 + l32;
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) {
+    for (int t = 0; t < KSTEPS; ++t) {
+      if constexpr (QBF) {
+        const int ch = 2 * t + h;
+        kf[kb][t] = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ swz_k16<D>(row)) << 4));
+      } else {
         const int ch = 4 * t + 2 * h;
         const i32x4 a0 = *(const lds_i32x4*)(Ks + row * D + ((ch ^ swz_k8<D>(row)) << 4));
         const i32x4 a1 = *(const lds_i32x4*)(Ks + row * D + (((ch + 1) ^ swz_k8<D>(row)) << 4));
@@ -136,15 +159,34 @@ struct Fp8Fwd {
     }
   }
 
-  __device__ __forceinline__ void qk() {
+  // S^T of 32-key block kb.
+  __device__ __forceinline__ void qk(int kb) {
+    sacc[kb] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t)
+    for (int t = 0; t < KSTEPS; ++t) {
+      if constexpr (QBF)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][t], qf[t], sacc[kb], 0, 0, 0);
+      else
         sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[kb][t], qf[t], sacc[kb], 0, 0,
                                                                    0, 0, 0, 0);
+    }
+  }
+  // K fragments and S^T of the whole tile; bf16 K is read and multiplied one
+  // 32-key block at a time, so only one block of fragments is live.
+  template <int ST>
+  __device__ __forceinline__ void read_k_qk() {
+    if constexpr (QBF) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        read_k<ST>(kb);
+        qk(kb);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) read_k<ST>(kb);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) qk(kb);
+    }
   }
 
   template <int PB>
@@ -160,7 +202,7 @@ struct Fp8Fwd {
   template <bool EDGE, int PB>
   __device__ __forceinline__ void softmax(int kt) {
     const int k0 = kt * BN;
-    const float c = cq * dk[k0 / 128];
+    const float c = QBF ? cq : cq * dk[k0 / 128];   // bf16 scores carry no descale
     const float dv_t = dv[k0 / 128];
     if constexpr (EDGE) {
 #pragma unroll
@@ -225,9 +267,8 @@ struct Fp8Fwd {
     sync_tiles();                           // K_j, V_{j-1} landed; iteration j-1 done
     issue_k<PB ^ 1>(j + 1);                 // unconditional: see the bf16 kernel
     issue_v<PB>(j);
-    read_k<PB>();
     if constexpr (!FIRST) read_v<PB ^ 1>();
-    qk();
+    read_k_qk<PB>();
     rescale();
     if constexpr (!FIRST) pv<PB ^ 1>();
     softmax<EDGE, PB>(j);
@@ -246,18 +287,22 @@ struct Fp8Fwd {
   }
 };
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2)
-void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
+// Q and K: E4M3 codes (uint8), or bf16 (uint16) when QBF. DQ and DK are
+// unused when QBF. The bf16-score instance at d = 128 needs more than the 256
+// registers of two waves per SIMD (bf16 Q and K fragments are twice the
+// size), so it runs one workgroup per CU with the whole register file.
+template <int D, bool QBF>
+__global__ __launch_bounds__(kThreads, (QBF && D == 128) ? 1 : 2)
+void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
                          const uint8_t* __restrict__ V, uint16_t* __restrict__ O,
                          float* __restrict__ LSE, const float* __restrict__ DQ,
                          const float* __restrict__ DK, const float* __restrict__ DV, int N,
                          int nqt, float c0, int causal, int window, int qsign) {
-  using S = Fp8Fwd<D>;
-  __shared__ __attribute__((aligned(1024))) char k0s[S::TILE];
-  __shared__ __attribute__((aligned(1024))) char k1s[S::TILE];
-  __shared__ __attribute__((aligned(1024))) char v0s[S::TILE];
-  __shared__ __attribute__((aligned(1024))) char v1s[S::TILE];
+  using S = Fp8Fwd<D, QBF>;
+  __shared__ __attribute__((aligned(1024))) char k0s[S::KTILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[S::KTILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[S::VTILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[S::VTILE];
 
   S st;
   st.kl[0] = (lds_char*)k0s;
@@ -278,34 +323,53 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
   st.qrow = tr.q0 + st.wave * 32 + st.l32;
   const size_t head = (size_t)tr.bh * N * D;
   const int nsb = (N + 127) / 128;             // scaling blocks per head
-  st.dk = DK + (size_t)tr.bh * nsb;
+  st.dk = QBF ? nullptr : DK + (size_t)tr.bh * nsb;
   st.dv = DV + (size_t)tr.bh * nsb;
-  st.cq = c0 * DQ[(size_t)tr.bh * nsb + tr.q0 / 128];
+  st.cq = QBF ? c0 : c0 * DQ[(size_t)tr.bh * nsb + tr.q0 / 128];
 
-  // Q fragments: lane holds q8[qrow][64t + 32h .. +31].
+  if constexpr (QBF) {
+    // Q fragments (bf16): lane holds q[qrow][16t + 8h .. +7].
+    const uint16_t* Q = (const uint16_t*)Qv;
 #pragma unroll
-  for (int t = 0; t < S::KSTEPS; ++t) {
-    i32x4 x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-    if (st.qrow < N) {
-      const uint8_t* p = Q + head + (size_t)st.qrow * D + 64 * t + 32 * st.h;
-      x0 = *(const i32x4*)p;
-      x1 = *(const i32x4*)(p + 16);
+    for (int t = 0; t < S::KSTEPS; ++t) {
+      i32x4 x = {0, 0, 0, 0};
+      if (st.qrow < N) x = *(const i32x4*)(Q + head + (size_t)st.qrow * D + 16 * t + 8 * st.h);
+      x ^= qsign;
+      st.qf[t] = __builtin_bit_cast(bf16x8, x);
     }
-    x0 ^= qsign;
-    x1 ^= qsign;
-    st.qf[t] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  } else {
+    // Q fragments (E4M3): lane holds q8[qrow][64t + 32h .. +31].
+    const uint8_t* Q = (const uint8_t*)Qv;
+#pragma unroll
+    for (int t = 0; t < S::KSTEPS; ++t) {
+      i32x4 x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
+      if (st.qrow < N) {
+        const uint8_t* p = Q + head + (size_t)st.qrow * D + 64 * t + 32 * st.h;
+        x0 = *(const i32x4*)p;
+        x1 = *(const i32x4*)(p + 16);
+      }
+      x0 ^= qsign;
+      x1 ^= qsign;
+      st.qf[t] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    }
   }
 
   // HBM -> LDS copies: LDS chunk p (p = 64 * block + lane) of the K image is
-  // row p / DCH, physical column p % DCH, holding logical column
-  // (p % DCH) ^ swizzle(row). The V image's LDS row r holds key v8_row(r).
-  st.kres = make_rsrc(K + head, (uint32_t)N * D);
+  // row p / KDCH, physical column p % KDCH, holding logical column
+  // (p % KDCH) ^ swizzle(row). The V image's LDS row r holds key v8_row(r).
+  st.kres = make_rsrc((const char*)Kv + head * S::KBYTES, (uint32_t)N * D * S::KBYTES);
   st.vres = make_rsrc(V + head, (uint32_t)N * D);
 #pragma unroll
-  for (int u = 0; u < S::LOADS; ++u) {
+  for (int u = 0; u < S::KLOADS; ++u) {
     const int p = (u * 4 + st.wave) * 64 + st.lane;
-    const int row = p / S::DCH, pc = p % S::DCH;
-    st.koff[u] = row * D + (pc ^ swz_k8<D>(row)) * 16;
+    const int row = p / S::KDCH, pc = p % S::KDCH;
+    if constexpr (QBF) st.koff[u] = row * D * 2 + (pc ^ swz_k16<D>(row)) * 16;
+    else st.koff[u] = row * D + (pc ^ swz_k8<D>(row)) * 16;
+  }
+#pragma unroll
+  for (int u = 0; u < S::VLOADS; ++u) {
+    const int p = (u * 4 + st.wave) * 64 + st.lane;
+    const int row = p / S::VDCH, pc = p % S::VDCH;
     st.voff[u] = v8_row(row) * D + (pc ^ swz_v8<D>(row)) * 16;
   }
 
@@ -362,21 +426,30 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
 
 }  // namespace
 
-hipError_t launch_attn_fwd_fp8(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool qk_bf16, hipStream_t stream) {
   const int nqt = (a.N + kBM - 1) / kBM;
   const int G = nqt * a.BH;  // bounded by the C ABI's shape checks
   const float c0 = fabsf(a.scale) * kLog2e;
-  const int qsign = a.scale < 0.f ? (int)0x80808080u : 0;
-  const uint8_t* q = (const uint8_t*)a.q;
-  const uint8_t* k = (const uint8_t*)a.k;
+  const bool neg = a.scale < 0.f;
   const uint8_t* v = (const uint8_t*)a.v;
   uint16_t* o = (uint16_t*)a.o;
-  if (a.d == 128)
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<128>, dim3(G), dim3(kThreads), 0, stream, q, k, v, o,
-                       a.lse, a.dq, a.dk, a.dv, a.N, nqt, c0, a.causal, a.window, qsign);
-  else
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<64>, dim3(G), dim3(kThreads), 0, stream, q, k, v, o,
-                       a.lse, a.dq, a.dk, a.dv, a.N, nqt, c0, a.causal, a.window, qsign);
+  if (qk_bf16) {
+    const int qsign = neg ? (int)0x80008000u : 0;
+    if (a.d == 128)
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, true>), dim3(G), dim3(kThreads), 0, stream, a.q,
+                         a.k, v, o, a.lse, a.dq, a.dk, a.dv, a.N, nqt, c0, a.causal, a.window, qsign);
+    else
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<64, true>), dim3(G), dim3(kThreads), 0, stream, a.q,
+                         a.k, v, o, a.lse, a.dq, a.dk, a.dv, a.N, nqt, c0, a.causal, a.window, qsign);
+  } else {
+    const int qsign = neg ? (int)0x80808080u : 0;
+    if (a.d == 128)
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false>), dim3(G), dim3(kThreads), 0, stream, a.q,
+                         a.k, v, o, a.lse, a.dq, a.dk, a.dv, a.N, nqt, c0, a.causal, a.window, qsign);
+    else
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<64, false>), dim3(G), dim3(kThreads), 0, stream, a.q,
+                         a.k, v, o, a.lse, a.dq, a.dk, a.dv, a.N, nqt, c0, a.causal, a.window, qsign);
+  }
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ using namespace mi355attn;
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 constexpr long long kMaxGrid = 2147483647LL;  // gridDim.x limit
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -42,37 +42,45 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   bool empty = false;
   int rc = check_shape(B, H, N, d, &empty);
   if (rc != ATTN_OK || empty) return rc;
-  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP8_E4M3) return ATTN_E_DTYPE;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP8_E4M3 && dtype != ATTN_DTYPE_FP8_PV)
+    return ATTN_E_DTYPE;
   if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
-  const bool fp8 = dtype == ATTN_DTYPE_FP8_E4M3;
+  const bool fp8 = dtype == ATTN_DTYPE_FP8_E4M3;   // all E4M3
+  const bool pv8 = dtype == ATTN_DTYPE_FP8_PV;     // q, k bf16; v E4M3
   if (fp8 && (!descale_q || !descale_k || !descale_v)) return ATTN_E_NULL;
+  if (pv8 && !descale_v) return ATTN_E_NULL;
   if (causal != 0 && causal != 1) return ATTN_E_WINDOW;
   if (window < -1) return ATTN_E_WINDOW;
   if (!isfinite(scale)) return ATTN_E_SCALE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return ATTN_E_ALIGN;
-  if (fp8 && (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4)))
-    return ATTN_E_ALIGN;
+  if (fp8 && (!aligned(descale_q, 4) || !aligned(descale_k, 4))) return ATTN_E_ALIGN;
+  if ((fp8 || pv8) && !aligned(descale_v, 4)) return ATTN_E_ALIGN;
 
   const size_t elems = (size_t)B * H * N * d;
-  const size_t in_bytes = elems * (fp8 ? 1 : 2);
+  const size_t qk_bytes = elems * (fp8 ? 1 : 2);
+  const size_t v_bytes = elems * (fp8 || pv8 ? 1 : 2);
   const size_t o_bytes = elems * 2;
   const size_t lse_bytes = (size_t)B * H * N * sizeof(float);
   const void* ins[3] = {q, k, v};
-  for (const void* in : ins) {
-    if (overlap(o, o_bytes, in, in_bytes) || overlap(lse, lse_bytes, in, in_bytes)) return ATTN_E_ALIAS;
+  const size_t in_bytes[3] = {qk_bytes, qk_bytes, v_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(o, o_bytes, ins[i], in_bytes[i]) || overlap(lse, lse_bytes, ins[i], in_bytes[i]))
+      return ATTN_E_ALIAS;
   }
   if (overlap(o, o_bytes, lse, lse_bytes)) return ATTN_E_ALIAS;
-  if (fp8) {
+  if (fp8 || pv8) {
     const size_t ds_bytes = (size_t)B * H * ((N + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS) * sizeof(float);
-    const void* dss[3] = {descale_q, descale_k, descale_v};
+    const void* dss[3] = {fp8 ? descale_q : nullptr, fp8 ? descale_k : nullptr, descale_v};
     for (const void* ds : dss)
-      if (overlap(o, o_bytes, ds, ds_bytes) || overlap(lse, lse_bytes, ds, ds_bytes)) return ATTN_E_ALIAS;
+      if (ds && (overlap(o, o_bytes, ds, ds_bytes) || overlap(lse, lse_bytes, ds, ds_bytes)))
+        return ATTN_E_ALIAS;
   }
 
-  FwdArgs a{q, k, v, o, lse, descale_q, descale_k, descale_v, B * H, N, d, causal, window, scale};
-  const hipError_t e = fp8 ? launch_attn_fwd_fp8(a, (hipStream_t)stream)
-                           : launch_attn_fwd_bf16(a, (hipStream_t)stream);
+  FwdArgs a{q, k, v, o, lse, fp8 ? descale_q : nullptr, fp8 ? descale_k : nullptr,
+            (fp8 || pv8) ? descale_v : nullptr, B * H, N, d, causal, window, scale};
+  const hipError_t e = (fp8 || pv8) ? launch_attn_fwd_fp8(a, pv8, (hipStream_t)stream)
+                                    : launch_attn_fwd_bf16(a, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
