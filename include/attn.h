@@ -115,6 +115,38 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, const float* descale_q, const float* descale_k,
              const float* descale_v, void* stream);
 
+/* Largest number of partial results attn_lse_merge accepts. */
+#define ATTN_MAX_MERGE 4096
+
+/*
+ * attn_lse_merge - merge R partial results computed over disjoint key sets.
+ *
+ * For every row (b, h, i), partial r holds o_r, the softmax over its own key
+ * set applied to V, and lse_r, the natural log of that set's softmax
+ * denominator (as attn_fwd writes them). The merged row is
+ *   lse = ln sum_r exp(lse_r)
+ *   o   = sum_r exp(lse_r - lse) * o_r
+ * the update of the running statistics and output of the online softmax
+ * ([WGC] section 2) taken across partial results, which a split of the keys
+ * over workgroups or devices needs ([YT] section 2.3.1). Partials with
+ * lse_r = -inf carry no weight; a row whose partials are all -inf gets o = 0
+ * and lse = -inf. Inputs holding NaN or +inf give undefined rows.
+ *
+ *   o_part    fp32 [R][B][H][N][d], read only.
+ *   lse_part  fp32 [R][B][H][N], read only.
+ *   o         bf16 [B][H][N][d] output (fp32 sums, rounded to nearest even).
+ *   lse       fp32 [B][H][N] output.
+ *   R         number of partials, 1 .. ATTN_MAX_MERGE.
+ *   d         64, 128 or 256.
+ *   stream    hipStream_t or NULL. The call only enqueues one kernel.
+ * All pointers are device pointers owned by the caller; tensors 16-byte
+ * aligned, fp32 LSE arrays 4-byte aligned. Outputs may not overlap inputs or
+ * each other. B*H*N = 0 is an empty problem (ATTN_OK, nothing enqueued).
+ * Returns ATTN_OK or an ATTN_E_* code.
+ */
+int attn_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+                   int R, int B, int H, int N, int d, void* stream);
+
 /*
  * attn_fp8_quantize - bf16 -> E4M3 with one scaling factor per 128-row block.
  *

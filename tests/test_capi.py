@@ -38,14 +38,15 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert set(names) == {"attn_fwd", "attn_fp8_quantize", "attn_strerror", "attn_version"}
+    assert set(names) == {"attn_fwd", "attn_fp8_quantize", "attn_lse_merge", "attn_strerror",
+                          "attn_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(tafa.SIGNATURES)
 
 
 def test_version_and_strerror(lib):
-    assert tafa.version() == 10100
+    assert tafa.version() == 10200
     codes = header_codes()
     assert codes["ATTN_OK"] == 0
     texts = {tafa.strerror(c) for c in codes.values()}
@@ -156,3 +157,26 @@ def test_binding_checks_before_calling(lib):
         tafa.fwd(q, q, q)                        # CPU tensors are refused by the binding
     with pytest.raises(ValueError):
         tafa.quantize(q)
+
+
+def call_merge(lib, op=A, lp=A + GAP, o=A + 2 * GAP, lse=A + 3 * GAP, R=3, B=2, H=3, N=300, d=128):
+    return lib.attn_lse_merge(op, lp, o, lse, R, B, H, N, d, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=0), "ATTN_E_SHAPE"), (dict(R=4097), "ATTN_E_SHAPE"), (dict(B=-1), "ATTN_E_SHAPE"),
+    (dict(N=(1 << 23) + 1), "ATTN_E_SHAPE"),
+    (dict(d=32), "ATTN_E_HEADDIM"), (dict(d=96), "ATTN_E_HEADDIM"),
+    (dict(op=None), "ATTN_E_NULL"), (dict(lp=None), "ATTN_E_NULL"), (dict(o=None), "ATTN_E_NULL"),
+    (dict(lse=None), "ATTN_E_NULL"),
+    (dict(op=A + 4), "ATTN_E_ALIGN"), (dict(o=A + 2 * GAP + 8), "ATTN_E_ALIGN"),
+    (dict(lp=A + GAP + 2), "ATTN_E_ALIGN"), (dict(lse=A + 3 * GAP + 1), "ATTN_E_ALIGN"),
+    (dict(o=A + 1024), "ATTN_E_ALIAS"), (dict(lse=A + GAP + 64), "ATTN_E_ALIAS"),
+    (dict(lse=A + 2 * GAP + 4096), "ATTN_E_ALIAS"),
+])
+def test_lse_merge_rejects(lib, kw, code):
+    assert call_merge(lib, **kw) == E[code]
+
+
+def test_lse_merge_empty_problem_is_ok(lib):
+    assert call_merge(lib, N=0, op=None, d=77) == E["ATTN_OK"]

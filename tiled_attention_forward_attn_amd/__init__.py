@@ -36,6 +36,7 @@ _f = ctypes.c_float
 SIGNATURES = {
     "attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp]),
     "attn_fp8_quantize": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "attn_lse_merge": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "attn_strerror": (ctypes.c_char_p, [_i]),
     "attn_version": (_i, []),
 }
@@ -155,5 +156,30 @@ def quantize(x: torch.Tensor, per_tensor: bool = False, out: torch.Tensor | None
     return out, descale
 
 
-__all__ = ["fwd", "quantize", "load", "strerror", "version", "AttnError", "LIB_PATH",
+def merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: torch.Tensor | None = None,
+          lse: torch.Tensor | None = None, stream=None):
+    """Merge partial results over disjoint key sets through attn_lse_merge.
+
+    o_parts fp32 [R, B, H, N, d], lse_parts fp32 [R, B, H, N] (natural-log
+    softmax denominators) -> (o bf16 [B, H, N, d], lse fp32 [B, H, N])."""
+    if o_parts.dim() != 5 or lse_parts.dim() != 4 or o_parts.shape[:4] != lse_parts.shape:
+        raise ValueError("o_parts must be [R, B, H, N, d] and lse_parts [R, B, H, N]")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("o_parts and lse_parts must be fp32")
+    for name, t in (("o_parts", o_parts), ("lse_parts", lse_parts)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    R, B, H, N, d = o_parts.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    rc = load().attn_lse_merge(_ptr(o_parts), _ptr(lse_parts), _ptr(out), _ptr(lse), R, B, H, N, d,
+                               _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_lse_merge")
+    return out, lse
+
+
+__all__ = ["fwd", "quantize", "merge", "load", "strerror", "version", "AttnError", "LIB_PATH",
            "SIGNATURES", "BLOCK_ROWS", "DTYPE_BF16", "DTYPE_FP8_E4M3", "DTYPE_FP8_PV"]

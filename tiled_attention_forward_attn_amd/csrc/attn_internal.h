@@ -27,6 +27,9 @@ struct FwdArgs {
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 // qk_bf16: q and k are bf16 (S = Q K^T on bf16 MFMAs), v stays E4M3.
 hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool qk_bf16, hipStream_t stream);
+// rows = B * H * N; d in {64, 128, 256}.
+hipError_t launch_lse_merge(const float* o_part, const float* lse_part, int R, long long rows, int d,
+                            void* o, float* lse, hipStream_t stream);
 hipError_t launch_fp8_quantize(const void* x, void* x8, float* descale, int BH, int N, int d,
                                int per_tensor, hipStream_t stream);
 

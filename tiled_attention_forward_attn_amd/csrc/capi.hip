@@ -11,7 +11,7 @@ using namespace mi355attn;
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
 constexpr long long kMaxGrid = 2147483647LL;  // gridDim.x limit
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -99,6 +99,30 @@ extern "C" int attn_fp8_quantize(const void* x_bf16, void* x_fp8, float* descale
     return ATTN_E_ALIAS;
   const hipError_t e = launch_fp8_quantize(x_bf16, x_fp8, descale, B * H, N, d, per_tensor,
                                            (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+extern "C" int attn_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+                              int R, int B, int H, int N, int d, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || R < 1 || R > ATTN_MAX_MERGE) return ATTN_E_SHAPE;
+  const long long rows = (long long)B * H * N;
+  if (rows == 0) return ATTN_OK;
+  if ((long long)B * H > ATTN_MAX_BH || N > ATTN_MAX_N) return ATTN_E_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return ATTN_E_HEADDIM;
+  // one workgroup per 256 / (d / 4) rows must fit the 1-D grid
+  if ((rows + 256 / (d / 4) - 1) / (256 / (d / 4)) > kMaxGrid) return ATTN_E_SHAPE;
+  if (!o_part || !lse_part || !o || !lse) return ATTN_E_NULL;
+  if (!aligned(o_part, 16) || !aligned(o, 16) || !aligned(lse_part, 4) || !aligned(lse, 4))
+    return ATTN_E_ALIGN;
+  const size_t op_bytes = (size_t)R * rows * d * sizeof(float);
+  const size_t lp_bytes = (size_t)R * rows * sizeof(float);
+  const size_t o_bytes = (size_t)rows * d * 2;
+  const size_t lse_bytes = (size_t)rows * sizeof(float);
+  if (overlap(o, o_bytes, o_part, op_bytes) || overlap(o, o_bytes, lse_part, lp_bytes) ||
+      overlap(lse, lse_bytes, o_part, op_bytes) || overlap(lse, lse_bytes, lse_part, lp_bytes) ||
+      overlap(o, o_bytes, lse, lse_bytes))
+    return ATTN_E_ALIAS;
+  const hipError_t e = launch_lse_merge(o_part, lse_part, R, rows, d, o, lse, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
