@@ -32,6 +32,8 @@
 #ifndef MI355_ATTN_H
 #define MI355_ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -55,7 +57,8 @@ enum {
   ATTN_E_WINDOW = -6,    /* window < -1, or causal not 0/1                            */
   ATTN_E_ALIAS = -7,     /* an output overlaps an input or another output             */
   ATTN_E_LAUNCH = -8,    /* the kernel launch failed (no device, bad stream, ...)     */
-  ATTN_E_SCALE = -9      /* scale is not finite                                       */
+  ATTN_E_SCALE = -9,     /* scale is not finite                                       */
+  ATTN_E_WORKSPACE = -10 /* decode workspace NULL, misaligned or too small            */
 };
 
 /* Largest supported sizes (index arithmetic is 64-bit; these bound the grid). */
@@ -146,6 +149,49 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int attn_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
                    int R, int B, int H, int N, int d, void* stream);
+
+/* Most queries per (batch, head) attn_decode takes: one 32-wide MFMA block. */
+#define ATTN_MAX_DECODE_Q 32
+
+/*
+ * attn_decode_workspace_bytes - device workspace attn_decode needs:
+ * splits * B * H * Nq * (4 d + 4) bytes (the fp32 partial outputs and their
+ * log-sum-exps). Returns 0 for arguments attn_decode would reject.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int Nq, int d, int splits);
+
+/*
+ * attn_decode - attention of Nq <= 32 new queries against Nk >= Nq cached
+ * keys and values of the same sequences (decoding with a key/value cache,
+ * [JJ] section 3). The queries are the last Nq positions: query i sits at
+ * position Nk - Nq + i and, with causal = 1, attends keys j <= Nk - Nq + i.
+ *   s_ij = scale * <q_i, k_j>;  o_i = sum_j softmax_j(s_i) v_j;
+ *   lse_i = ln sum_j exp(s_ij)
+ * The keys of every (b, h) are split into `splits` contiguous chunks of
+ * ceil(Nk / splits) keys (rounded up to the 32- or 64-key tile); each chunk's
+ * tiled online softmax ([WGC] sections 1-2) writes an fp32 partial into the
+ * workspace, and the partials are merged as attn_lse_merge does. Two kernels
+ * on `stream`; nothing is allocated.
+ *
+ *   q         bf16 [B][H][Nq][d]; k, v bf16 [B][H][Nk][d]. Read only.
+ *   o         bf16 [B][H][Nq][d] output; lse fp32 [B][H][Nq] output.
+ *   Nq        1 .. ATTN_MAX_DECODE_Q (0: empty problem); Nk: Nq .. ATTN_MAX_N.
+ *   d         64 or 128.
+ *   causal    0 or 1 (bottom-right aligned, as above).
+ *   scale     finite; 0 and negative allowed.
+ *   splits    1 .. ATTN_MAX_MERGE key chunks per (b, h); more chunks give more
+ *             workgroups (B * H * splits) for small batches.
+ *   workspace device memory of at least attn_decode_workspace_bytes(B, H, Nq,
+ *             d, splits) bytes, 16-byte aligned, owned by the caller; its
+ *             contents are scratch.
+ * Pointers are device pointers owned by the caller; tensors 16-byte aligned,
+ * lse 4-byte aligned; outputs and workspace may not overlap inputs or each
+ * other. Returns ATTN_OK or an ATTN_E_* code (ATTN_E_WORKSPACE: workspace
+ * NULL, misaligned or too small).
+ */
+int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int Nq, int Nk, int d, int causal, float scale, int splits,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_fp8_quantize - bf16 -> E4M3 with one scaling factor per 128-row block.

@@ -12,6 +12,8 @@ Modules
              recurrence, both fp64
   fp8        the OCP E4M3FN number format and the per-block / per-tensor
              quantiser, from the format definition
+  decode     attention of a few queries against a longer key/value sequence
+             (the last positions, bottom-right causal alignment), fp64
   merge      the merge of partial results over disjoint key sets (their
              log-sum-exp weighted combination), fp64
   metrics    the error measures used to compare a result with the oracle
@@ -29,6 +31,7 @@ from .attention import (allowed_range, attention_two_pass, attention_online,
                         probabilities, attention_rows)
 from .fp8 import (E4M3_MAX, e4m3_decode_table, e4m3_decode, e4m3_encode,
                   quantize, dequantize, QUANT_BLOCK_ROWS)
+from .decode import attention_decode
 from .merge import lse_merge
 from .metrics import max_abs, l1_rel, rmse_rel
 
@@ -36,5 +39,5 @@ __all__ = [
     "allowed_range", "attention_two_pass", "attention_online", "probabilities",
     "attention_rows", "E4M3_MAX", "e4m3_decode_table", "e4m3_decode",
     "e4m3_encode", "quantize", "dequantize", "QUANT_BLOCK_ROWS", "max_abs",
-    "l1_rel", "rmse_rel", "lse_merge",
+    "l1_rel", "rmse_rel", "lse_merge", "attention_decode",
 ]

@@ -38,15 +38,15 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert set(names) == {"attn_fwd", "attn_fp8_quantize", "attn_lse_merge", "attn_strerror",
-                          "attn_version"}
+    assert set(names) == {"attn_fwd", "attn_fp8_quantize", "attn_lse_merge", "attn_decode",
+                          "attn_decode_workspace_bytes", "attn_strerror", "attn_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(tafa.SIGNATURES)
 
 
 def test_version_and_strerror(lib):
-    assert tafa.version() == 10200
+    assert tafa.version() == 10300
     codes = header_codes()
     assert codes["ATTN_OK"] == 0
     texts = {tafa.strerror(c) for c in codes.values()}
@@ -180,3 +180,41 @@ def test_lse_merge_rejects(lib, kw, code):
 
 def test_lse_merge_empty_problem_is_ok(lib):
     assert call_merge(lib, N=0, op=None, d=77) == E["ATTN_OK"]
+
+
+WS = A + 5 * GAP
+
+
+def call_decode(lib, q=A, k=A + GAP, v=A + 2 * GAP, o=A + 3 * GAP, lse=A + 4 * GAP, B=2, H=3,
+                Nq=4, Nk=1000, d=128, causal=1, scale=0.125, splits=8, ws=WS, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_workspace_bytes(B, H, Nq, d, splits)
+    return lib.attn_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, splits, ws, ws_bytes, None)
+
+
+def test_decode_workspace_bytes(lib):
+    assert lib.attn_decode_workspace_bytes(2, 3, 4, 128, 8) == 8 * 2 * 3 * 4 * (4 * 128 + 4)
+    assert lib.attn_decode_workspace_bytes(1, 1, 1, 64, 1) == 64 * 4 + 4
+    for args in ((2, 3, 33, 128, 8), (2, 3, 4, 96, 8), (2, 3, 4, 128, 0), (-1, 3, 4, 128, 8),
+                 (2, 3, 0, 128, 8)):
+        assert lib.attn_decode_workspace_bytes(*args) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Nq=33), "ATTN_E_SHAPE"), (dict(Nk=3), "ATTN_E_SHAPE"), (dict(splits=0), "ATTN_E_SHAPE"),
+    (dict(splits=4097), "ATTN_E_SHAPE"), (dict(B=-1), "ATTN_E_SHAPE"), (dict(Nk=(1 << 23) + 1), "ATTN_E_SHAPE"),
+    (dict(d=256, ws_bytes=1 << 30), "ATTN_E_HEADDIM"),
+    (dict(q=None), "ATTN_E_NULL"), (dict(v=None), "ATTN_E_NULL"), (dict(lse=None), "ATTN_E_NULL"),
+    (dict(causal=2), "ATTN_E_WINDOW"), (dict(scale=math.inf), "ATTN_E_SCALE"),
+    (dict(k=A + GAP + 8), "ATTN_E_ALIGN"), (dict(lse=A + 4 * GAP + 2), "ATTN_E_ALIGN"),
+    (dict(ws=None), "ATTN_E_WORKSPACE"), (dict(ws=WS + 8), "ATTN_E_WORKSPACE"),
+    (dict(ws_bytes=16), "ATTN_E_WORKSPACE"),
+    (dict(o=A + GAP + 4096), "ATTN_E_ALIAS"), (dict(ws=A + 2 * GAP + 1024), "ATTN_E_ALIAS"),
+    (dict(lse=WS + 64), "ATTN_E_ALIAS"), (dict(o=A + 4 * GAP - 64), "ATTN_E_ALIAS"),
+])
+def test_decode_rejects(lib, kw, code):
+    assert call_decode(lib, **kw) == E[code]
+
+
+def test_decode_empty_problem_is_ok(lib):
+    assert call_decode(lib, Nq=0, q=None, ws=None, ws_bytes=0) == E["ATTN_OK"]

@@ -37,6 +37,9 @@ SIGNATURES = {
     "attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp]),
     "attn_fp8_quantize": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "attn_lse_merge": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "attn_decode_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
+    "attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
+                         ctypes.c_size_t, _vp]),
     "attn_strerror": (ctypes.c_char_p, [_i]),
     "attn_version": (_i, []),
 }
@@ -181,5 +184,50 @@ def merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: torch.Tensor | No
     return out, lse
 
 
-__all__ = ["fwd", "quantize", "merge", "load", "strerror", "version", "AttnError", "LIB_PATH",
+MAX_DECODE_Q = 32
+
+
+def default_splits(B: int, H: int, Nk: int) -> int:
+    """Key chunks per (b, h) for attn_decode: about 2048 single-wave
+    workgroups in all, each chunk at least 256 keys."""
+    return max(1, min(-(-2048 // max(1, B * H)), -(-Nk // 256), 4096))
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+           scale: float | None = None, splits: int | None = None,
+           workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+           lse: torch.Tensor | None = None, stream=None):
+    """Decode attention through attn_decode: q bf16 [B, H, Nq, d] (Nq <= 32,
+    the sequence's last positions) against k, v bf16 [B, H, Nk, d].
+    Returns (o bf16 [B, H, Nq, d], lse fp32 [B, H, Nq]). The workspace (device
+    bytes) is allocated here when not given."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_4d(name, t)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if splits is None:
+        splits = default_splits(B, H, Nk)
+    lib = load()
+    need = lib.attn_decode_workspace_bytes(B, H, Nq, d, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    rc = lib.attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d,
+                         int(causal), float(scale), int(splits), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_decode")
+    return out, lse
+
+
+__all__ = ["fwd", "quantize", "merge", "decode", "default_splits", "load", "strerror", "version", "AttnError", "LIB_PATH",
            "SIGNATURES", "BLOCK_ROWS", "DTYPE_BF16", "DTYPE_FP8_E4M3", "DTYPE_FP8_PV"]

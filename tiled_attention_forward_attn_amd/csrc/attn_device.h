@@ -9,6 +9,7 @@ namespace mi355attn {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
@@ -62,6 +63,26 @@ template <int N>
 __device__ __forceinline__ void wait_vmem_upto() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16-byte chunk swizzles of bf16 K and V tiles in LDS (rows of 2 D bytes).
+// K is read 16 B per lane from 32 consecutive rows at one chunk column; V is
+// read 8 B per lane as 4 consecutive rows x 32 bytes per 16-lane group by the
+// transposing read. The XOR keeps both conflict-free for 32- and 64-bank LDS
+// organisations.
+template <int D>
+__device__ __forceinline__ int bf16_swz_k(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return ((r >> 1) & 7) ^ ((r & 1) << 2);
+}
+template <int D>
+__device__ __forceinline__ int bf16_swz_v(int r) {
+  if constexpr (D == 128) {
+    const int p = r & 3;
+    return ((p << 1) + (p >> 1)) << 1;
+  } else {
+    return (r & 3) << 1;
+  }
 }
 
 // Bijective remap of the hardware workgroup id so that ids dispatched to the

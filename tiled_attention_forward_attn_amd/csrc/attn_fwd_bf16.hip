@@ -50,25 +50,6 @@ namespace {
 
 constexpr float kRescaleSlack = 8.f;   // see the header comment
 
-// 16-byte chunk swizzles. K is read 16 B per lane from 32 consecutive rows at
-// one chunk column; V is read 8 B per lane as 4 consecutive rows x 32 bytes per
-// 16-lane group by the transposing read. The XOR keeps both conflict-free for
-// 32- and 64-bank LDS organisations.
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  if constexpr (D == 128) return r & 15;
-  else return ((r >> 1) & 7) ^ ((r & 1) << 2);
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int r) {
-  if constexpr (D == 128) {
-    const int p = r & 3;
-    return ((p << 1) + (p >> 1)) << 1;
-  } else {
-    return (r & 3) << 1;
-  }
-}
-
 template <int D, int BN, int QB>
 struct Bf16Fwd {
   static constexpr int DCH = D / 8;                     // 16-byte chunks per row
@@ -125,7 +106,7 @@ struct Bf16Fwd {
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
         const int ch = 2 * t + h;
-        kf[kb][t] = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ swz_k<D>(row)) << 4));
+        kf[kb][t] = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ bf16_swz_k<D>(row)) << 4));
       }
     }
   }
@@ -142,8 +123,8 @@ struct Bf16Fwd {
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
         const int col = db * 32 + 16 * (g & 1) + 4 * (sl & 3);
-        const int a1 = r1 * D * 2 + (((col >> 3) ^ swz_v<D>(r1)) << 4) + ((col >> 2) & 1) * 8;
-        const int a2 = r2 * D * 2 + (((col >> 3) ^ swz_v<D>(r2)) << 4) + ((col >> 2) & 1) * 8;
+        const int a1 = r1 * D * 2 + (((col >> 3) ^ bf16_swz_v<D>(r1)) << 4) + ((col >> 2) & 1) * 8;
+        const int a2 = r2 * D * 2 + (((col >> 3) ^ bf16_swz_v<D>(r2)) << 4) + ((col >> 2) & 1) * 8;
         const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + a1));
         const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + a2));
         vf[s][db] = __builtin_bit_cast(bf16x8, i16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1],
@@ -371,8 +352,8 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   for (int u = 0; u < S::LOADS; ++u) {
     const int p = (u * 4 + st.wave) * 64 + st.lane;
     const int row = p / S::DCH, pc = p % S::DCH;
-    st.koff[u] = (row * D + (pc ^ swz_k<D>(row)) * 8) * 2;
-    st.voff[u] = (row * D + (pc ^ swz_v<D>(row)) * 8) * 2;
+    st.koff[u] = (row * D + (pc ^ bf16_swz_k<D>(row)) * 8) * 2;
+    st.voff[u] = (row * D + (pc ^ bf16_swz_v<D>(row)) * 8) * 2;
   }
 
 #pragma unroll

@@ -53,13 +53,6 @@ __device__ __forceinline__ int swz_v8(int r) {
   if constexpr (D == 128) return r & 7;
   else return (r >> 1) & 3;
 }
-// 16-byte chunk swizzle of a bf16 K tile (rows of 2 D bytes), read 16 B per
-// lane from 32 consecutive rows at one chunk column.
-template <int D>
-__device__ __forceinline__ int swz_k16(int r) {
-  if constexpr (D == 128) return r & 15;
-  else return ((r >> 1) & 7) ^ ((r & 1) << 2);
-}
 // LDS row of key offset k within a tile: swap bits 2 and 3 (an involution).
 __device__ __forceinline__ int v8_row(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
@@ -130,7 +123,7 @@ struct Fp8Fwd {
     for (int t = 0; t < KSTEPS; ++t) {
       if constexpr (QBF) {
         const int ch = 2 * t + h;
-        kf[kb][t] = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ swz_k16<D>(row)) << 4));
+        kf[kb][t] = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ bf16_swz_k<D>(row)) << 4));
       } else {
         const int ch = 4 * t + 2 * h;
         const i32x4 a0 = *(const lds_i32x4*)(Ks + row * D + ((ch ^ swz_k8<D>(row)) << 4));
@@ -363,7 +356,7 @@ void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ K
   for (int u = 0; u < S::KLOADS; ++u) {
     const int p = (u * 4 + st.wave) * 64 + st.lane;
     const int row = p / S::KDCH, pc = p % S::KDCH;
-    if constexpr (QBF) st.koff[u] = row * D * 2 + (pc ^ swz_k16<D>(row)) * 16;
+    if constexpr (QBF) st.koff[u] = row * D * 2 + (pc ^ bf16_swz_k<D>(row)) * 16;
     else st.koff[u] = row * D + (pc ^ swz_k8<D>(row)) * 16;
   }
 #pragma unroll

@@ -24,7 +24,23 @@ struct FwdArgs {
   float scale;
 };
 
+// Decode launch parameters, validated by the C ABI.
+struct DecodeArgs {
+  const void* q;     // bf16 [BH][Nq][d]
+  const void* k;     // bf16 [BH][Nk][d]
+  const void* v;
+  void* o;           // bf16 [BH][Nq][d]
+  float* lse;        // [BH][Nq]
+  void* workspace;   // fp32 partials [splits][BH * Nq][d], then lse [splits][BH * Nq]
+  int BH, Nq, Nk, d, causal, splits;
+  float scale;
+};
+
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream);
+size_t decode_workspace_bytes(long long rows, int d, int splits);
+// Keys per split: ceil(Nk / splits) rounded up to the key tile.
+int decode_chunk(int Nk, int d, int splits);
 // qk_bf16: q and k are bf16 (S = Q K^T on bf16 MFMAs), v stays E4M3.
 hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool qk_bf16, hipStream_t stream);
 // rows = B * H * N; d in {64, 128, 256}.

@@ -11,7 +11,7 @@ using namespace mi355attn;
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
 constexpr long long kMaxGrid = 2147483647LL;  // gridDim.x limit
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -126,11 +126,66 @@ extern "C" int attn_lse_merge(const float* o_part, const float* lse_part, void* 
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
+namespace {
+
+// Shape checks of attn_decode; *empty is set for B*H*Nq == 0.
+int check_decode(int B, int H, int Nq, int Nk, int d, int splits, bool* empty) {
+  if (B < 0 || H < 0 || Nq < 0 || Nq > ATTN_MAX_DECODE_Q || Nk < Nq || Nk > ATTN_MAX_N ||
+      splits < 1 || splits > ATTN_MAX_MERGE)
+    return ATTN_E_SHAPE;
+  *empty = (long long)B * H * Nq == 0;
+  if (*empty) return ATTN_OK;
+  if ((long long)B * H > ATTN_MAX_BH) return ATTN_E_SHAPE;
+  if (d != 64 && d != 128) return ATTN_E_HEADDIM;
+  if ((long long)B * H * splits > kMaxGrid) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" size_t attn_decode_workspace_bytes(int B, int H, int Nq, int d, int splits) {
+  bool empty = false;
+  if (check_decode(B, H, Nq, Nq, d, splits, &empty) != ATTN_OK || empty) return 0;
+  return decode_workspace_bytes((long long)B * H * Nq, d, splits);
+}
+
+extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                           int splits, void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_decode(B, H, Nq, Nk, d, splits, &empty);
+  if (rc != ATTN_OK || empty) return rc;
+  if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+  if (causal != 0 && causal != 1) return ATTN_E_WINDOW;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return ATTN_E_ALIGN;
+  const long long rows = (long long)B * H * Nq;
+  const size_t need = decode_workspace_bytes(rows, d, splits);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return ATTN_E_WORKSPACE;
+  const size_t q_bytes = (size_t)rows * d * 2;
+  const size_t kv_bytes = (size_t)B * H * Nk * d * 2;
+  const size_t lse_bytes = (size_t)rows * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  const size_t in_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(o, q_bytes, ins[i], in_bytes[i]) || overlap(lse, lse_bytes, ins[i], in_bytes[i]) ||
+        overlap(workspace, need, ins[i], in_bytes[i]))
+      return ATTN_E_ALIAS;
+  }
+  if (overlap(o, q_bytes, lse, lse_bytes) || overlap(o, q_bytes, workspace, need) ||
+      overlap(lse, lse_bytes, workspace, need))
+    return ATTN_E_ALIAS;
+  DecodeArgs a{q, k, v, o, lse, workspace, B * H, Nq, Nk, d, causal, splits, scale};
+  const hipError_t e = launch_attn_decode(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
 extern "C" const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";
     case ATTN_E_NULL: return "a required pointer is NULL";
-    case ATTN_E_SHAPE: return "B, H or N is negative or beyond the supported maximum";
+    case ATTN_E_SHAPE: return "a size (B, H, N, Nq, Nk, R, splits) is out of range";
     case ATTN_E_HEADDIM: return "head dimension d must be 64 or 128";
     case ATTN_E_DTYPE: return "unknown dtype or quantisation mode";
     case ATTN_E_ALIGN: return "a tensor pointer is misaligned (16 bytes for tensors, 4 for fp32 arrays)";
@@ -138,6 +193,7 @@ extern "C" const char* attn_strerror(int code) {
     case ATTN_E_ALIAS: return "an output buffer overlaps an input or another output";
     case ATTN_E_LAUNCH: return "kernel launch failed (no usable GPU or invalid stream)";
     case ATTN_E_SCALE: return "scale must be finite";
+    case ATTN_E_WORKSPACE: return "decode workspace is NULL, misaligned or smaller than attn_decode_workspace_bytes";
     default: return "unknown error code";
   }
 }

@@ -23,8 +23,6 @@ namespace {
 
 constexpr int kMergeThreads = 256;
 
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-
 template <int D>
 __global__ __launch_bounds__(kMergeThreads)
 void lse_merge_kernel(const float* __restrict__ op, const float* __restrict__ lp, int R,
