@@ -51,7 +51,7 @@ enum {
   ATTN_OK = 0,
   ATTN_E_NULL = -1,      /* a required pointer is NULL                               */
   ATTN_E_SHAPE = -2,     /* B, H or N negative or beyond the supported maximum        */
-  ATTN_E_HEADDIM = -3,   /* d not in {64, 128}                                        */
+  ATTN_E_HEADDIM = -3,   /* d not supported by the call (64, 128; 256 where stated)   */
   ATTN_E_DTYPE = -4,     /* unknown dtype, or fp8 descale pointers missing            */
   ATTN_E_ALIGN = -5,     /* a tensor pointer is not 16-byte aligned (lse: 4-byte)     */
   ATTN_E_WINDOW = -6,    /* window < -1, or causal not 0/1                            */
@@ -88,7 +88,8 @@ enum {
  *             even at the end: [WGC] section 3).
  *   lse       [B][H][N] fp32 output, may NOT be NULL.
  *   B, H, N   batch, heads, sequence length (queries = keys = N).
- *   d         head dimension, 64 or 128 ([WGC] "适用场景": d = 64 or 128).
+ *   d         head dimension: 64 or 128 ([WGC] "适用场景"); 256 with dtype 0
+ *             ([WGC] "后续方向" lists it as the next step).
  *   causal    1: key j allowed only if j <= i. 0: no causal cut.
  *   window    -1: no window. w >= 0: keys with i - w <= j <= i (causal) or
  *             |i - j| <= w (non-causal): the band of [YT] section 2.1.2, both

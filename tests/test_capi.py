@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strerror(lib):
-    assert tafa.version() == 10300
+    assert tafa.version() == 10400
     codes = header_codes()
     assert codes["ATTN_OK"] == 0
     texts = {tafa.strerror(c) for c in codes.values()}
@@ -74,7 +74,9 @@ E = header_codes()
 @pytest.mark.parametrize("kw,code", [
     (dict(B=-1), "ATTN_E_SHAPE"), (dict(H=-2), "ATTN_E_SHAPE"), (dict(N=-5), "ATTN_E_SHAPE"),
     (dict(N=(1 << 23) + 1), "ATTN_E_SHAPE"), (dict(B=1 << 13, H=1 << 12), "ATTN_E_SHAPE"),
-    (dict(d=96), "ATTN_E_HEADDIM"), (dict(d=256), "ATTN_E_HEADDIM"), (dict(d=0), "ATTN_E_HEADDIM"),
+    (dict(d=96), "ATTN_E_HEADDIM"), (dict(d=512), "ATTN_E_HEADDIM"), (dict(d=0), "ATTN_E_HEADDIM"),
+    (dict(d=256, dtype=1, dq=A + 5 * GAP, dk=A + 6 * GAP, dv=A + 7 * GAP), "ATTN_E_HEADDIM"),
+    (dict(d=256, dtype=2, dv=A + 7 * GAP), "ATTN_E_HEADDIM"),
     (dict(dtype=3), "ATTN_E_DTYPE"), (dict(dtype=-1), "ATTN_E_DTYPE"),
     (dict(q=None), "ATTN_E_NULL"), (dict(k=None), "ATTN_E_NULL"), (dict(v=None), "ATTN_E_NULL"),
     (dict(o=None), "ATTN_E_NULL"), (dict(lse=None), "ATTN_E_NULL"),
@@ -135,7 +137,7 @@ def call_quant(lib, x=A, x8=A + GAP, ds=A + 2 * GAP, B=2, H=3, N=300, d=128, per
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=-1), "ATTN_E_SHAPE"), (dict(N=(1 << 23) + 1), "ATTN_E_SHAPE"),
-    (dict(d=32), "ATTN_E_HEADDIM"),
+    (dict(d=32), "ATTN_E_HEADDIM"), (dict(d=256), "ATTN_E_HEADDIM"),
     (dict(x=None), "ATTN_E_NULL"), (dict(x8=None), "ATTN_E_NULL"), (dict(ds=None), "ATTN_E_NULL"),
     (dict(per_tensor=2), "ATTN_E_DTYPE"),
     (dict(x=A + 8), "ATTN_E_ALIGN"), (dict(x8=A + GAP + 4), "ATTN_E_ALIGN"),

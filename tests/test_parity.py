@@ -394,3 +394,37 @@ def test_fp8pv_outlier_workload_meets_the_bar(lib):
     print(f"outlier workload RMSE/RMS vs unquantised oracle: fp8 PV {r_pv:.4f}, all-E4M3 {r_all:.4f}")
     assert r_pv <= FP8_RMSE_REL
     assert r_pv < r_all
+
+
+# ---- head dimension 256 (bf16 only)
+
+@pytest.mark.parametrize("B,H,N", [(1, 1, 1), (1, 2, 127), (2, 1, 300), (1, 1, 1000)])
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 100), (False, 70), (True, 0)])
+def test_bf16_d256(lib, B, H, N, causal, window):
+    d = 256
+    q, k, v = make_qkv(B, H, N, d, seed=300 + N)
+    scale = 1 / math.sqrt(d)
+    o, lse = lib.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, window=window, scale=scale)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = attention_two_pass(q, k, v, scale, causal, window)
+    check_bf16(o, lse, ref_o, ref_lse, f"d256 {(B, H, N, causal, window)}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2])
+def test_bf16_d256_scales(lib, scale):
+    q, k, v = make_qkv(1, 1, 200, 256, seed=310)
+    o, lse = lib.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    check_bf16(o, lse, *attention_two_pass(q, k, v, scale, True, -1), f"d256 scale={scale}")
+
+
+def test_bf16_d256_larger_sampled(lib):
+    B, H, N, d = 2, 4, 4096, 256
+    q, k, v = make_qkv(B, H, N, d, seed=320)
+    scale = 1 / math.sqrt(d)
+    o, lse = lib.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, window=1500, scale=scale)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (1, 3)]:
+        rows = sampled_rows(N, 300, 330 + b + h)
+        ref_o, ref_lse = attention_rows(q[b, h], k[b, h], v[b, h], scale, True, 1500, rows)
+        check_bf16(o[b, h, rows], lse[b, h, rows], ref_o, ref_lse, f"d256 head {(b, h)}")

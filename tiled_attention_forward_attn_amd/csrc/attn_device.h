@@ -70,14 +70,16 @@ __device__ __forceinline__ void wait_vmem_upto() {
 // read 8 B per lane as 4 consecutive rows x 32 bytes per 16-lane group by the
 // transposing read. The XOR keeps both conflict-free for 32- and 64-bank LDS
 // organisations.
+// At D = 256 a row is 512 bytes, which maps onto the banks like a 256-byte
+// row (bank = byte offset mod 256), so the D = 128 patterns carry over.
 template <int D>
 __device__ __forceinline__ int bf16_swz_k(int r) {
-  if constexpr (D == 128) return r & 15;
+  if constexpr (D >= 128) return r & 15;
   else return ((r >> 1) & 7) ^ ((r & 1) << 2);
 }
 template <int D>
 __device__ __forceinline__ int bf16_swz_v(int r) {
-  if constexpr (D == 128) {
+  if constexpr (D >= 128) {
     const int p = r & 3;
     return ((p << 1) + (p >> 1)) << 1;
   } else {

@@ -299,7 +299,7 @@ struct Bf16Fwd {
 };
 
 template <int D, int BN, int QB>
-__global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1)
+__global__ __launch_bounds__(kThreads, (QB == 1 && D <= 128) ? 2 : 1)
 void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                           float* __restrict__ LSE, int N, int nqt, float c, int causal,
@@ -416,6 +416,10 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 // Configuration per head dimension: queries per wave (32 QB) and keys per tile.
 constexpr int kQB128 = 1, kBN128 = 32;
 constexpr int kQB64 = 1, kBN64 = 64;
+// d = 256: 128 accumulator floats per lane and 64-register Q, K and V
+// fragment sets need more than the 256 registers of two waves per SIMD; one
+// workgroup per CU gets the whole register file.
+constexpr int kQB256 = 1, kBN256 = 32;
 
 }  // namespace
 
@@ -429,6 +433,10 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.d == 128) {
     const int nqt = (a.N + 128 * kQB128 - 1) / (128 * kQB128);
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, kBN128, kQB128>), dim3(nqt * a.BH), dim3(kThreads),
+                       0, stream, q, k, v, o, a.lse, a.N, nqt, c, a.causal, a.window, qsign);
+  } else if (a.d == 256) {
+    const int nqt = (a.N + 128 * kQB256 - 1) / (128 * kQB256);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<256, kBN256, kQB256>), dim3(nqt * a.BH), dim3(kThreads),
                        0, stream, q, k, v, o, a.lse, a.N, nqt, c, a.causal, a.window, qsign);
   } else {
     const int nqt = (a.N + 128 * kQB64 - 1) / (128 * kQB64);

@@ -11,7 +11,7 @@ using namespace mi355attn;
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
 constexpr long long kMaxGrid = 2147483647LL;  // gridDim.x limit
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -21,13 +21,14 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
-// Shape checks shared by both entry points; *empty is set for B*H*N == 0.
-int check_shape(int B, int H, int N, int d, bool* empty) {
+// Shape checks shared by attn_fwd and attn_fp8_quantize; *empty is set for
+// B*H*N == 0. d = 256 only where d256 is set (the bf16 path).
+int check_shape(int B, int H, int N, int d, bool d256, bool* empty) {
   if (B < 0 || H < 0 || N < 0) return ATTN_E_SHAPE;
   *empty = (long long)B * H * N == 0;
   if (*empty) return ATTN_OK;
   if (N > ATTN_MAX_N || (long long)B * H > ATTN_MAX_BH) return ATTN_E_SHAPE;
-  if (d != 64 && d != 128) return ATTN_E_HEADDIM;
+  if (d != 64 && d != 128 && !(d256 && d == 256)) return ATTN_E_HEADDIM;
   // one workgroup per 128-row block of every head must fit the 1-D grid
   if ((long long)((N + 127) / 128) * B * H > kMaxGrid) return ATTN_E_SHAPE;
   return ATTN_OK;
@@ -40,7 +41,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                         int dtype, const float* descale_q, const float* descale_k,
                         const float* descale_v, void* stream) {
   bool empty = false;
-  int rc = check_shape(B, H, N, d, &empty);
+  int rc = check_shape(B, H, N, d, dtype == ATTN_DTYPE_BF16, &empty);
   if (rc != ATTN_OK || empty) return rc;
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP8_E4M3 && dtype != ATTN_DTYPE_FP8_PV)
     return ATTN_E_DTYPE;
@@ -87,7 +88,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
 extern "C" int attn_fp8_quantize(const void* x_bf16, void* x_fp8, float* descale, int B, int H,
                                  int N, int d, int per_tensor, void* stream) {
   bool empty = false;
-  int rc = check_shape(B, H, N, d, &empty);
+  int rc = check_shape(B, H, N, d, false, &empty);
   if (rc != ATTN_OK || empty) return rc;
   if (!x_bf16 || !x_fp8 || !descale) return ATTN_E_NULL;
   if (per_tensor != 0 && per_tensor != 1) return ATTN_E_DTYPE;
@@ -186,7 +187,7 @@ extern "C" const char* attn_strerror(int code) {
     case ATTN_OK: return "success";
     case ATTN_E_NULL: return "a required pointer is NULL";
     case ATTN_E_SHAPE: return "a size (B, H, N, Nq, Nk, R, splits) is out of range";
-    case ATTN_E_HEADDIM: return "head dimension d must be 64 or 128";
+    case ATTN_E_HEADDIM: return "head dimension d not supported here (64 or 128; 256 for bf16 attn_fwd and attn_lse_merge)";
     case ATTN_E_DTYPE: return "unknown dtype or quantisation mode";
     case ATTN_E_ALIGN: return "a tensor pointer is misaligned (16 bytes for tensors, 4 for fp32 arrays)";
     case ATTN_E_WINDOW: return "causal must be 0 or 1 and window must be >= -1";
