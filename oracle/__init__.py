@@ -16,6 +16,8 @@ Modules
              (the last positions, bottom-right causal alignment), fp64
   merge      the merge of partial results over disjoint key sets (their
              log-sum-exp weighted combination), fp64
+  paged      decode attention against a paged key/value cache: the block
+             table's page gather, then the decode oracle
   metrics    the error measures used to compare a result with the oracle
 
 Sources (web pages on FlashAttention-3, cited by title and section):
@@ -23,8 +25,8 @@ Sources (web pages on FlashAttention-3, cited by title and section):
   [JJ]   "大模型加速-核心网络算子-Flash Attention V3"
   [YT]   "FlashAttention V3：优化框架吞吐量的关键技术实践"
 
-Every function in this package is pinned by tests in ``tests/test_oracle.py``
-and ``tests/test_fp8_model.py`` against library routines, closed forms,
+Every function in this package is pinned by tests (``tests/test_oracle*.py``
+and ``tests/test_fp8_model.py``) against library routines, closed forms,
 invariants and brute force; none is "parity unpinned".
 """
 from .attention import (allowed_range, attention_two_pass, attention_online,
@@ -32,6 +34,7 @@ from .attention import (allowed_range, attention_two_pass, attention_online,
 from .fp8 import (E4M3_MAX, e4m3_decode_table, e4m3_decode, e4m3_encode,
                   quantize, dequantize, QUANT_BLOCK_ROWS)
 from .decode import attention_decode
+from .paged import attention_decode_paged, gather_pages
 from .merge import lse_merge
 from .metrics import max_abs, l1_rel, rmse_rel
 
@@ -39,5 +42,6 @@ __all__ = [
     "allowed_range", "attention_two_pass", "attention_online", "probabilities",
     "attention_rows", "E4M3_MAX", "e4m3_decode_table", "e4m3_decode",
     "e4m3_encode", "quantize", "dequantize", "QUANT_BLOCK_ROWS", "max_abs",
-    "l1_rel", "rmse_rel", "lse_merge", "attention_decode",
+    "l1_rel", "rmse_rel", "lse_merge", "attention_decode", "attention_decode_paged",
+    "gather_pages",
 ]
