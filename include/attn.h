@@ -194,6 +194,55 @@ int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse
                 int B, int H, int Nq, int Nk, int d, int causal, float scale, int splits,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Page sizes (positions per page) attn_decode_paged takes: powers of two in
+ * this range, so a 32-key tile never spans two pages. */
+#define ATTN_MIN_PAGE 32
+#define ATTN_MAX_PAGE 4096
+
+/*
+ * attn_decode_paged - attn_decode against a paged key/value cache (the
+ * PagedAttention cache management that [WGC] "limitations and follow-up
+ * directions" names as a next step). Sequence b's cached positions live in
+ * pages of page_size positions scattered over a shared pool; position p of
+ * sequence b is row p % page_size of page block_table[b][p / page_size].
+ * Sequence b holds seq_lens[b] valid positions, and its Nq queries are its
+ * last Nq positions (query i at seq_lens[b] - Nq + i, causal as in
+ * attn_decode). Per (b, h) the result is attn_decode's over the gathered
+ * seq_lens[b] positions; each sequence's keys are split into `splits` chunks
+ * of its own length. Two kernels on `stream`; nothing is allocated; no host
+ * synchronisation (block_table and seq_lens are read on the device).
+ *
+ *   q            bf16 [B][H][Nq][d]. Read only.
+ *   k_cache,
+ *   v_cache      bf16 pools [num_pages][H][page_size][d] (one page holds every
+ *                head's rows for its positions). Read only.
+ *   block_table  int32 [B][max_pages], device memory: physical page of each
+ *                logical page. Entries past a sequence's last page are unused.
+ *   seq_lens     int32 [B], device memory: valid positions per sequence; the
+ *                caller keeps Nq <= seq_lens[b] <= max_pages * page_size.
+ *   o, lse       outputs as in attn_decode.
+ *   Nq           1 .. ATTN_MAX_DECODE_Q (0: empty problem); d: 64 or 128.
+ *   num_pages    pages in each pool (>= 1); page_size: a power of two in
+ *                [ATTN_MIN_PAGE, ATTN_MAX_PAGE]; max_pages >= 1 with
+ *                max_pages * page_size <= ATTN_MAX_N.
+ *   causal, scale, splits, workspace, workspace_bytes: as in attn_decode
+ *                (workspace size from attn_decode_workspace_bytes).
+ * Device-side values outside the contract cannot make the kernel access
+ * memory outside the pools, the table row or the outputs: a table entry
+ * outside [0, num_pages) reads as a page of zeros, seq_lens[b] is clamped to
+ * [0, max_pages * page_size], and rows past seq_lens[b] are never read. The
+ * results for such inputs are unspecified; seq_lens[b] = 0 gives o = 0,
+ * lse = -inf. Pointers are device pointers owned by the caller; tensors
+ * 16-byte aligned, lse, block_table and seq_lens 4-byte aligned; outputs and
+ * workspace may not overlap inputs or each other. Returns ATTN_OK or an
+ * ATTN_E_* code.
+ */
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int* block_table, const int* seq_lens, void* o, float* lse,
+                      int B, int H, int Nq, int d, int num_pages, int page_size, int max_pages,
+                      int causal, float scale, int splits, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /*
  * attn_fp8_quantize - bf16 -> E4M3 with one scaling factor per 128-row block.
  *

@@ -39,14 +39,15 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
     assert set(names) == {"attn_fwd", "attn_fp8_quantize", "attn_lse_merge", "attn_decode",
-                          "attn_decode_workspace_bytes", "attn_strerror", "attn_version"}
+                          "attn_decode_workspace_bytes", "attn_decode_paged", "attn_strerror",
+                          "attn_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(tafa.SIGNATURES)
 
 
 def test_version_and_strerror(lib):
-    assert tafa.version() == 10400
+    assert tafa.version() == 10500
     codes = header_codes()
     assert codes["ATTN_OK"] == 0
     texts = {tafa.strerror(c) for c in codes.values()}
@@ -220,3 +221,36 @@ def test_decode_rejects(lib, kw, code):
 
 def test_decode_empty_problem_is_ok(lib):
     assert call_decode(lib, Nq=0, q=None, ws=None, ws_bytes=0) == E["ATTN_OK"]
+
+
+def call_paged(lib, q=A, kc=A + GAP, vc=A + 2 * GAP, table=A + 6 * GAP, lens=A + 7 * GAP,
+               o=A + 3 * GAP, lse=A + 4 * GAP, B=2, H=3, Nq=4, d=128, num_pages=100, page_size=64,
+               max_pages=40, causal=1, scale=0.125, splits=8, ws=WS, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_workspace_bytes(B, H, Nq, d, splits)
+    return lib.attn_decode_paged(q, kc, vc, table, lens, o, lse, B, H, Nq, d, num_pages, page_size,
+                                 max_pages, causal, scale, splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page_size=16), "ATTN_E_SHAPE"), (dict(page_size=96), "ATTN_E_SHAPE"),
+    (dict(page_size=8192), "ATTN_E_SHAPE"), (dict(num_pages=0), "ATTN_E_SHAPE"),
+    (dict(max_pages=0), "ATTN_E_SHAPE"), (dict(max_pages=(1 << 23) // 64 + 1), "ATTN_E_SHAPE"),
+    (dict(Nq=33), "ATTN_E_SHAPE"), (dict(splits=0), "ATTN_E_SHAPE"), (dict(B=-1), "ATTN_E_SHAPE"),
+    (dict(d=256, ws_bytes=1 << 30), "ATTN_E_HEADDIM"),
+    (dict(q=None), "ATTN_E_NULL"), (dict(kc=None), "ATTN_E_NULL"), (dict(table=None), "ATTN_E_NULL"),
+    (dict(lens=None), "ATTN_E_NULL"), (dict(lse=None), "ATTN_E_NULL"),
+    (dict(causal=2), "ATTN_E_WINDOW"), (dict(scale=math.nan), "ATTN_E_SCALE"),
+    (dict(vc=A + 2 * GAP + 8), "ATTN_E_ALIGN"), (dict(table=A + 6 * GAP + 2), "ATTN_E_ALIGN"),
+    (dict(lens=A + 7 * GAP + 1), "ATTN_E_ALIGN"),
+    (dict(ws=None), "ATTN_E_WORKSPACE"), (dict(ws_bytes=16), "ATTN_E_WORKSPACE"),
+    (dict(o=A + GAP + 4096), "ATTN_E_ALIAS"), (dict(lse=A + 6 * GAP + 16), "ATTN_E_ALIAS"),
+    (dict(ws=A + 7 * GAP), "ATTN_E_ALIAS"), (dict(o=A + 4 * GAP - 64), "ATTN_E_ALIAS"),
+])
+def test_decode_paged_rejects(lib, kw, code):
+    assert call_paged(lib, **kw) == E[code]
+
+
+def test_decode_paged_empty_problem_is_ok(lib):
+    assert call_paged(lib, Nq=0, q=None, ws=None, ws_bytes=0) == E["ATTN_OK"]
+    assert call_paged(lib, B=0, table=None, lens=None, ws=None, ws_bytes=0) == E["ATTN_OK"]

@@ -40,6 +40,8 @@ SIGNATURES = {
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
                          ctypes.c_size_t, _vp]),
+    "attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                               _f, _i, _vp, ctypes.c_size_t, _vp]),
     "attn_strerror": (ctypes.c_char_p, [_i]),
     "attn_version": (_i, []),
 }
@@ -229,5 +231,55 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = 
     return out, lse
 
 
-__all__ = ["fwd", "quantize", "merge", "decode", "default_splits", "load", "strerror", "version", "AttnError", "LIB_PATH",
+def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_table: torch.Tensor, seq_lens: torch.Tensor, *, causal: bool = False,
+                 scale: float | None = None, splits: int | None = None,
+                 workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None, stream=None):
+    """Decode attention through attn_decode_paged: q bf16 [B, H, Nq, d] against
+    the paged pools k_cache, v_cache bf16 [num_pages, H, page_size, d], with
+    block_table int32 [B, max_pages] and seq_lens int32 [B] on the device.
+    Returns (o bf16 [B, H, Nq, d], lse fp32 [B, H, Nq]). splits defaults to the
+    value for the longest sequence the table can address."""
+    _check_4d("q", q)
+    _check_4d("k_cache", k_cache)
+    _check_4d("v_cache", v_cache)
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16")
+    B, H, Nq, d = q.shape
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[2]
+    if k_cache.shape != (num_pages, H, page_size, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [num_pages, H, page_size, d] with q's H and d")
+    for name, t, shape in (("block_table", block_table, None), ("seq_lens", seq_lens, (B,))):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous int32 tensor on q's device")
+        if shape is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if splits is None:
+        splits = default_splits(B, H, max_pages * page_size)
+    lib = load()
+    need = lib.attn_decode_workspace_bytes(B, H, Nq, d, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    rc = lib.attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                               _ptr(seq_lens), _ptr(out), _ptr(lse), B, H, Nq, d, num_pages,
+                               page_size, max_pages, int(causal), float(scale), int(splits),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_decode_paged")
+    return out, lse
+
+
+__all__ = ["fwd", "quantize", "merge", "decode", "decode_paged", "default_splits", "load", "strerror", "version", "AttnError", "LIB_PATH",
            "SIGNATURES", "BLOCK_ROWS", "DTYPE_BF16", "DTYPE_FP8_E4M3", "DTYPE_FP8_PV"]

@@ -18,13 +18,24 @@
 // buffer (tile t+1 in flight while tile t is multiplied), so waves never
 // wait for each other and the kernel has no barrier. One wave per workgroup
 // lets up to five waves with their copies in flight share a CU.
+//
+// Paged cache (the PagedAttention cache management that [WGC] lists among its
+// follow-up directions): the keys and values of a sequence sit in fixed-size
+// pages of a shared pool [num_pages][H][page_size][d], and the sequence's
+// block table names the page holding each run of page_size positions. The
+// page size is a power of two no smaller than the 32-key tile, so a tile lies
+// in one page: per tile one scalar table read, then a buffer descriptor over
+// exactly that tile's rows, so the same copies and LDS layout serve both
+// caches. Rows past the sequence (stale page contents) and table entries
+// outside the pool read as zero through the descriptor's range check; no
+// table content can make the kernel read outside the pool.
 #include "attn_device.h"
 #include "attn_internal.h"
 
 namespace mi355attn {
 namespace {
 
-template <int D, int BN>
+template <int D, int BN, bool PAGED>
 struct DecodeWave {
   static constexpr int DCH = D / 8;          // 16-byte chunks per row
   static constexpr int KSTEPS = D / 16;
@@ -41,6 +52,11 @@ struct DecodeWave {
   float c;
   i32x4 kres, vres;
   int koff[LOADS], voff[LOADS];
+  // paged cache: pool base, this sequence's block table row and this head
+  const uint16_t* kpool;
+  const uint16_t* vpool;
+  const int* table;
+  int head, H, page_shift, num_pages;
   bf16x8 qf[KSTEPS];
   f32x16 oacc[DBLK];
   f32x16 sacc[NKB];
@@ -49,7 +65,27 @@ struct DecodeWave {
 
   template <int ST>
   __device__ __forceinline__ void issue(int t) {
-    const int soff = (int)((uint32_t)t * TILE);
+    int soff = (int)((uint32_t)t * TILE);
+    if constexpr (PAGED) {
+      // descriptors over tile t's rows of its page; zero rows past k_hi
+      const int p0 = t * BN;
+      uint32_t bytes = 0;
+      const uint16_t* kb = kpool;
+      const uint16_t* vb = vpool;
+      if (p0 < k_hi) {
+        const int page = __builtin_amdgcn_readfirstlane(table[p0 >> page_shift]);
+        if ((unsigned)page < (unsigned)num_pages) {
+          const size_t row = ((size_t)page * H + head) * ((size_t)1 << page_shift) +
+                             (p0 & ((1 << page_shift) - 1));
+          kb = kpool + row * D;
+          vb = vpool + row * D;
+          bytes = (uint32_t)min(BN, k_hi - p0) * D * 2;
+        }
+      }
+      kres = make_rsrc(kb, bytes);
+      vres = make_rsrc(vb, bytes);
+      soff = 0;
+    }
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       copy_to_lds16(kres, kl[ST] + u * 1024, koff[u], soff);
@@ -142,14 +178,23 @@ struct DecodeWave {
   }
 };
 
+// Paged cache description (kernel argument).
+struct PagedCache {
+  const int* block_table;   // [B][max_pages]
+  const int* seq_lens;      // [B]
+  int H, num_pages, page_shift, max_pages;
+};
+
 // One wave per workgroup; workgroup w owns (bh, chunk) = (w / S, w % S).
-template <int D, int BN>
+// Contiguous cache: K, V [BH][Nk][d] and a fixed chunk. Paged: K, V are the
+// pools, Nk and the chunk come from the sequence's length.
+template <int D, int BN, bool PAGED>
 __global__ __launch_bounds__(64)
 void attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, float* __restrict__ OP,
                         float* __restrict__ LP, int Nq, int Nk, int S, int chunk, float c,
-                        int causal, int qsign, long long rows) {
-  using W = DecodeWave<D, BN>;
+                        int causal, int qsign, long long rows, PagedCache pc) {
+  using W = DecodeWave<D, BN, PAGED>;
   __shared__ __attribute__((aligned(1024))) char tiles[4 * W::TILE];
   W st;
   st.kl[0] = (lds_char*)tiles;
@@ -157,6 +202,21 @@ void attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   st.vl[0] = (lds_char*)tiles + 2 * W::TILE;
   st.vl[1] = (lds_char*)tiles + 3 * W::TILE;
   const int bh = blockIdx.x / S, sp = blockIdx.x % S;
+  if constexpr (PAGED) {
+    // this sequence's valid length, at most what its block table can address
+    const int b = bh / pc.H;
+    st.head = bh % pc.H;
+    st.H = pc.H;
+    st.page_shift = pc.page_shift;
+    st.num_pages = pc.num_pages;
+    st.table = pc.block_table + (size_t)b * pc.max_pages;
+    st.kpool = K;
+    st.vpool = V;
+    const int len = __builtin_amdgcn_readfirstlane(pc.seq_lens[b]);
+    Nk = max(0, min(len, pc.max_pages << pc.page_shift));
+    const int per = (Nk + S - 1) / S;
+    chunk = (per + BN - 1) / BN * BN;
+  }
   st.Nq = Nq;
   st.Nk = Nk;
   st.causal = causal;
@@ -167,7 +227,7 @@ void attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   st.qrow = st.l32;
   const int k_lo = sp * chunk;
   st.k_hi = min(Nk, k_lo + chunk);
-  const size_t qhead = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
+  const size_t qhead = (size_t)bh * Nq * D, khead = PAGED ? 0 : (size_t)bh * Nk * D;
 
 #pragma unroll
   for (int t = 0; t < W::KSTEPS; ++t) {
@@ -182,8 +242,10 @@ void attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   st.l = 0.f;
 
   if (k_lo < st.k_hi) {
-    st.kres = make_rsrc(K + khead, (uint32_t)Nk * D * 2);
-    st.vres = make_rsrc(V + khead, (uint32_t)Nk * D * 2);
+    if constexpr (!PAGED) {
+      st.kres = make_rsrc(K + khead, (uint32_t)Nk * D * 2);
+      st.vres = make_rsrc(V + khead, (uint32_t)Nk * D * 2);
+    }
 #pragma unroll
     for (int u = 0; u < W::LOADS; ++u) {
       const int p = u * 64 + st.lane;
@@ -242,17 +304,31 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {
   float* lp = op + (size_t)a.splits * rows * a.d;
   const float c = fabsf(a.scale) * kLog2e;
   const int qsign = a.scale < 0.f ? (int)0x80008000u : 0;
-  const int chunk = decode_chunk(a.Nk, a.d, a.splits);
   const dim3 grid((unsigned)((long long)a.BH * a.splits));
   const uint16_t* q = (const uint16_t*)a.q;
   const uint16_t* k = (const uint16_t*)a.k;
   const uint16_t* v = (const uint16_t*)a.v;
-  if (a.d == 128)
-    hipLaunchKernelGGL((attn_decode_kernel<128, 32>), grid, dim3(64), 0, stream, q, k, v, op, lp,
-                       a.Nq, a.Nk, a.splits, chunk, c, a.causal, qsign, rows);
-  else
-    hipLaunchKernelGGL((attn_decode_kernel<64, 64>), grid, dim3(64), 0, stream, q, k, v, op, lp,
-                       a.Nq, a.Nk, a.splits, chunk, c, a.causal, qsign, rows);
+  if (a.block_table) {
+    // paged: 32-key tiles at both head sizes (a tile never spans two pages)
+    int shift = 0;
+    while ((1 << shift) < a.page_size) ++shift;
+    const PagedCache pc{a.block_table, a.seq_lens, a.H, a.num_pages, shift, a.max_pages};
+    if (a.d == 128)
+      hipLaunchKernelGGL((attn_decode_kernel<128, 32, true>), grid, dim3(64), 0, stream, q, k, v, op,
+                         lp, a.Nq, 0, a.splits, 0, c, a.causal, qsign, rows, pc);
+    else
+      hipLaunchKernelGGL((attn_decode_kernel<64, 32, true>), grid, dim3(64), 0, stream, q, k, v, op,
+                         lp, a.Nq, 0, a.splits, 0, c, a.causal, qsign, rows, pc);
+  } else {
+    const int chunk = decode_chunk(a.Nk, a.d, a.splits);
+    const PagedCache none{nullptr, nullptr, 1, 0, 0, 0};
+    if (a.d == 128)
+      hipLaunchKernelGGL((attn_decode_kernel<128, 32, false>), grid, dim3(64), 0, stream, q, k, v, op,
+                         lp, a.Nq, a.Nk, a.splits, chunk, c, a.causal, qsign, rows, none);
+    else
+      hipLaunchKernelGGL((attn_decode_kernel<64, 64, false>), grid, dim3(64), 0, stream, q, k, v, op,
+                         lp, a.Nq, a.Nk, a.splits, chunk, c, a.causal, qsign, rows, none);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_lse_merge(op, lp, a.splits, rows, a.d, a.o, a.lse, stream);

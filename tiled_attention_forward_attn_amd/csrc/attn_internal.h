@@ -27,13 +27,17 @@ struct FwdArgs {
 // Decode launch parameters, validated by the C ABI.
 struct DecodeArgs {
   const void* q;     // bf16 [BH][Nq][d]
-  const void* k;     // bf16 [BH][Nk][d]
+  const void* k;     // bf16 [BH][Nk][d], or the paged pool [num_pages][H][page_size][d]
   const void* v;
   void* o;           // bf16 [BH][Nq][d]
   float* lse;        // [BH][Nq]
   void* workspace;   // fp32 partials [splits][BH * Nq][d], then lse [splits][BH * Nq]
   int BH, Nq, Nk, d, causal, splits;
   float scale;
+  // paged cache (block_table == nullptr: contiguous k, v)
+  const int* block_table = nullptr;   // [B][max_pages]
+  const int* seq_lens = nullptr;      // [B]
+  int H = 1, num_pages = 0, page_size = 0, max_pages = 0;
 };
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);

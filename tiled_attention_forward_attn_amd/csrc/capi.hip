@@ -11,7 +11,7 @@ using namespace mi355attn;
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;
 constexpr long long kMaxGrid = 2147483647LL;  // gridDim.x limit
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -182,11 +182,57 @@ extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o,
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
+extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                 const int* block_table, const int* seq_lens, void* o, float* lse,
+                                 int B, int H, int Nq, int d, int num_pages, int page_size,
+                                 int max_pages, int causal, float scale, int splits,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_decode(B, H, Nq, Nq, d, splits, &empty);
+  if (rc != ATTN_OK || empty) return rc;
+  if (page_size < ATTN_MIN_PAGE || page_size > ATTN_MAX_PAGE || (page_size & (page_size - 1)) ||
+      num_pages < 1 || max_pages < 1 || (long long)max_pages * page_size > ATTN_MAX_N ||
+      (long long)num_pages * H * page_size > (1LL << 40))
+    return ATTN_E_SHAPE;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return ATTN_E_NULL;
+  if (causal != 0 && causal != 1) return ATTN_E_WINDOW;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return ATTN_E_ALIGN;
+  const long long rows = (long long)B * H * Nq;
+  const size_t need = decode_workspace_bytes(rows, d, splits);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return ATTN_E_WORKSPACE;
+  const size_t q_bytes = (size_t)rows * d * 2;
+  const size_t pool_bytes = (size_t)num_pages * H * page_size * d * 2;
+  const size_t lse_bytes = (size_t)rows * sizeof(float);
+  const void* ins[5] = {q, k_cache, v_cache, block_table, seq_lens};
+  const size_t in_bytes[5] = {q_bytes, pool_bytes, pool_bytes,
+                              (size_t)B * max_pages * sizeof(int), (size_t)B * sizeof(int)};
+  for (int i = 0; i < 5; ++i) {
+    if (overlap(o, q_bytes, ins[i], in_bytes[i]) || overlap(lse, lse_bytes, ins[i], in_bytes[i]) ||
+        overlap(workspace, need, ins[i], in_bytes[i]))
+      return ATTN_E_ALIAS;
+  }
+  if (overlap(o, q_bytes, lse, lse_bytes) || overlap(o, q_bytes, workspace, need) ||
+      overlap(lse, lse_bytes, workspace, need))
+    return ATTN_E_ALIAS;
+  DecodeArgs a{q, k_cache, v_cache, o, lse, workspace, B * H, Nq, 0, d, causal, splits, scale};
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.H = H;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.max_pages = max_pages;
+  const hipError_t e = launch_attn_decode(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
 extern "C" const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";
     case ATTN_E_NULL: return "a required pointer is NULL";
-    case ATTN_E_SHAPE: return "a size (B, H, N, Nq, Nk, R, splits) is out of range";
+    case ATTN_E_SHAPE: return "a size (B, H, N, Nq, Nk, R, splits, page_size, num_pages, max_pages) is out of range";
     case ATTN_E_HEADDIM: return "head dimension d not supported here (64 or 128; 256 for bf16 attn_fwd and attn_lse_merge)";
     case ATTN_E_DTYPE: return "unknown dtype or quantisation mode";
     case ATTN_E_ALIGN: return "a tensor pointer is misaligned (16 bytes for tensors, 4 for fp32 arrays)";
