@@ -135,6 +135,25 @@ def check_workload_heads(o, lse, w, heads, rows_per_head):
         check_bf16(o[b, h, rows], lse[b, h, rows], ref_o, ref_lse, f"{w.name} head {(b, h)}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,causal,window", [(300, False, -1), (300, True, -1), (257, True, 40),
+                                             (512, False, 100), (260, True, 255), (513, True, -1)])
+def test_bf16_wide_grid(lib, d, N, causal, window):
+    # B * H * ceil(N / 256) >= 1024: at d = 128 without a window this selects
+    # the 8-wave workgroups (256 queries each); ragged N and every mask kind,
+    # compared on sampled heads
+    B, H = 32, 32
+    q, k, v = make_qkv(B, H, N, d, seed=N + d + window)
+    o, lse = lib.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, window=window)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    heads = [(0, 0), (5, 17), (31, 31), (16, 2)]
+    for b, h in heads:
+        ref_o, ref_lse = attention_two_pass(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                                            1 / math.sqrt(d), causal, window)
+        check_bf16(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ref_o, ref_lse, f"head {(b, h)}")
+
+
 @pytest.mark.parametrize("name", ["noncausal_b1h2n256d64_bf16", "causal_b4h16n2048d128_bf16"])
 def test_workload_full_compare(lib, name):
     w = BY_NAME[name]

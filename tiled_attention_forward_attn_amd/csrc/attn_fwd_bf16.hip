@@ -50,15 +50,17 @@ namespace {
 
 constexpr float kRescaleSlack = 8.f;   // see the header comment
 
-template <int D, int BN, int QB>
+template <int D, int BN, int QB, int NW>
 struct Bf16Fwd {
+  static constexpr int THREADS = 64 * NW;               // NW waves per workgroup
   static constexpr int DCH = D / 8;                     // 16-byte chunks per row
   static constexpr int KSTEPS = D / 16;                 // MFMA k-steps of QK^T
   static constexpr int DBLK = D / 32;                   // 32-wide d blocks of O^T
   static constexpr int NKB = BN / 32;                   // 32-key blocks of S^T
   static constexpr int PST = BN / 16;                   // 16-key MFMA steps of PV
   static constexpr int TILE = BN * D * 2;               // bytes of one K or V tile
-  static constexpr int LOADS = TILE / (16 * kThreads);  // 16-byte copies per thread
+  static constexpr int LOADS = TILE / (16 * THREADS);   // 16-byte copies per thread
+  static_assert(LOADS * 16 * THREADS == TILE, "tile must split into whole copies per thread");
   // Largest accepted sum of one lane's p without a new reference max: with
   // the exact step's slack every p <= 2^8, so this is never exceeded
   // right after it; it bounds every p by 16 NKB 2^8.
@@ -87,13 +89,13 @@ struct Bf16Fwd {
   __device__ __forceinline__ void issue_k(int kt) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
-      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff[u], (int)((uint32_t)kt * (BN * D * 2)));
+      copy_to_lds16(kres, kl[ST] + (u * NW + wave) * 1024, koff[u], (int)((uint32_t)kt * (BN * D * 2)));
   }
   template <int ST>
   __device__ __forceinline__ void issue_v(int kt) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
-      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff[u], (int)((uint32_t)kt * (BN * D * 2)));
+      copy_to_lds16(vres, vl[ST] + (u * NW + wave) * 1024, voff[u], (int)((uint32_t)kt * (BN * D * 2)));
   }
 
   // A operand of S^T = K Q^T: lane holds K[32 kb + l32][16 t + 8 h .. +7].
@@ -298,14 +300,14 @@ struct Bf16Fwd {
   }
 };
 
-template <int D, int BN, int QB>
-__global__ __launch_bounds__(kThreads, (QB == 1 && D <= 128) ? 2 : 1)
+template <int D, int BN, int QB, int NW>
+__global__ __launch_bounds__(64 * NW, (QB == 1 && D <= 128) ? 8 / NW : 1)
 void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                           float* __restrict__ LSE, int N, int nqt, float c, int causal,
                           int window, int qsign) {
-  using S = Bf16Fwd<D, BN, QB>;
-  constexpr int BMQ = 4 * 32 * QB;
+  using S = Bf16Fwd<D, BN, QB, NW>;
+  constexpr int BMQ = NW * 32 * QB;
   __shared__ __attribute__((aligned(1024))) char k0s[S::TILE];
   __shared__ __attribute__((aligned(1024))) char k1s[S::TILE];
   __shared__ __attribute__((aligned(1024))) char v0s[S::TILE];
@@ -350,7 +352,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   st.vres = make_rsrc(V + head, (uint32_t)N * D * 2);
 #pragma unroll
   for (int u = 0; u < S::LOADS; ++u) {
-    const int p = (u * 4 + st.wave) * 64 + st.lane;
+    const int p = (u * NW + st.wave) * 64 + st.lane;
     const int row = p / S::DCH, pc = p % S::DCH;
     st.koff[u] = (row * D + (pc ^ bf16_swz_k<D>(row)) * 8) * 2;
     st.voff[u] = (row * D + (pc ^ bf16_swz_v<D>(row)) * 8) * 2;
@@ -413,7 +415,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   }
 }
 
-// Configuration per head dimension: queries per wave (32 QB) and keys per tile.
+// Configuration per head dimension: queries per wave (32 QB), keys per tile.
 constexpr int kQB128 = 1, kBN128 = 32;
 constexpr int kQB64 = 1, kBN64 = 64;
 // d = 256: 128 accumulator floats per lane and 64-register Q, K and V
@@ -421,27 +423,36 @@ constexpr int kQB64 = 1, kBN64 = 64;
 // workgroup per CU gets the whole register file.
 constexpr int kQB256 = 1, kBN256 = 32;
 
+// Waves per workgroup at d = 128 (two waves per SIMD either way): one 8-wave
+// workgroup per CU copies each K/V tile into LDS once for 256 queries, half
+// the L2 -> LDS traffic and LDS writes of two 4-wave workgroups. Used without
+// a sliding window (a band cuts mask edges through more key tiles of a
+// 256-query tile) and when there are at least this many 256-query tiles, so
+// that the grid still fills the CUs and balances.
+constexpr long long kWideGridMin = 1024;
+
+template <int D, int BN, int QB, int NW>
+void launch_cfg(const FwdArgs& a, float c, int qsign, hipStream_t stream) {
+  const int rows = 32 * NW * QB;
+  const int nqt = (a.N + rows - 1) / rows;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BN, QB, NW>), dim3(nqt * a.BH), dim3(64 * NW), 0,
+                     stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.o, a.lse, a.N, nqt, c, a.causal, a.window, qsign);
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   const float c = fabsf(a.scale) * kLog2e;  // |scale| * log2(e)
   const int qsign = a.scale < 0.f ? (int)0x80008000u : 0;
-  const uint16_t* q = (const uint16_t*)a.q;
-  const uint16_t* k = (const uint16_t*)a.k;
-  const uint16_t* v = (const uint16_t*)a.v;
-  uint16_t* o = (uint16_t*)a.o;
+  const bool wide = a.window < 0 && (long long)((a.N + 255) / 256) * a.BH >= kWideGridMin;
   if (a.d == 128) {
-    const int nqt = (a.N + 128 * kQB128 - 1) / (128 * kQB128);
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, kBN128, kQB128>), dim3(nqt * a.BH), dim3(kThreads),
-                       0, stream, q, k, v, o, a.lse, a.N, nqt, c, a.causal, a.window, qsign);
+    if (wide) launch_cfg<128, kBN128, kQB128, 8>(a, c, qsign, stream);
+    else launch_cfg<128, kBN128, kQB128, 4>(a, c, qsign, stream);
   } else if (a.d == 256) {
-    const int nqt = (a.N + 128 * kQB256 - 1) / (128 * kQB256);
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<256, kBN256, kQB256>), dim3(nqt * a.BH), dim3(kThreads),
-                       0, stream, q, k, v, o, a.lse, a.N, nqt, c, a.causal, a.window, qsign);
+    launch_cfg<256, kBN256, kQB256, 4>(a, c, qsign, stream);
   } else {
-    const int nqt = (a.N + 128 * kQB64 - 1) / (128 * kQB64);
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, kBN64, kQB64>), dim3(nqt * a.BH), dim3(kThreads),
-                       0, stream, q, k, v, o, a.lse, a.N, nqt, c, a.causal, a.window, qsign);
+    launch_cfg<64, kBN64, kQB64, 4>(a, c, qsign, stream);
   }
   return hipGetLastError();
 }
