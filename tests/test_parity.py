@@ -291,6 +291,20 @@ def test_fp8_vs_dequantised_oracle(lib, B, H, N, d, causal, window, outliers):
                              f"{(B, H, N, d, causal, window, outliers)}", outliers)
 
 
+@pytest.mark.parametrize("N,causal", [(300, False), (300, True), (513, True)])
+def test_fp8_wide_grid(lib, N, causal):
+    # a large grid (B32 H32) with ragged N, checked on sampled heads against
+    # the bound above
+    B, H, d = 32, 32, 128
+    q, k, v = make_qkv(B, H, N, d, seed=60 + N)
+    scale = 1 / math.sqrt(d)
+    o, lse, codes = fp8_run(lib, q, k, v, False, causal, -1, scale)
+    for b, h in ((0, 0), (9, 30), (31, 31)):
+        sub = [c[b:b + 1, h:h + 1] for c in codes]
+        check_fp8_vs_dequantised(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], sub, scale, causal, -1,
+                                 f"wide {(N, causal)} head {(b, h)}", False)
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0])
 def test_fp8_scales(lib, scale):
     q, k, v = make_qkv(1, 1, 200, 128, seed=60)
