@@ -13,7 +13,8 @@
 //
 // The kernel is HBM-bound: each workgroup reads its block once (32 KiB at
 // d = 128) into registers with 16-byte coalesced loads, reduces the amax
-// across the workgroup, and writes 8 bytes of codes per 16 bytes read.
+// across the workgroup, and writes 8 bytes of codes per 16 bytes read; both
+// carry the nontemporal hint (streamed data, touched once).
 // Per-tensor mode (the naive baseline) needs a global amax first; it runs
 //   1. the same kernel in "amax only" mode, each block writing its amax into
 //      its own descale slot,
@@ -81,7 +82,7 @@ void fp8_quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
     const int chunk = tid + u * kThreads;
     const int row = rb * kRows + chunk / DCH, col = chunk % DCH;
     x[u] = i32x4{0, 0, 0, 0};
-    if (row < N) x[u] = *(const i32x4*)(X + head + (size_t)row * D + col * 8);
+    if (row < N) x[u] = __builtin_nontemporal_load((const i32x4*)(X + head + (size_t)row * D + col * 8));
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(x[u][e])), fabsf(bf16_hi(x[u][e]))));
@@ -108,7 +109,7 @@ void fp8_quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
                     sat(bf16_lo(x[u][1]) * r), sat(bf16_hi(x[u][1]) * r));
       out[1] = cvt4(sat(bf16_lo(x[u][2]) * r), sat(bf16_hi(x[u][2]) * r),
                     sat(bf16_lo(x[u][3]) * r), sat(bf16_hi(x[u][3]) * r));
-      *(i32x2*)(X8 + head + (size_t)row * D + col * 8) = out;
+      __builtin_nontemporal_store(out, (i32x2*)(X8 + head + (size_t)row * D + col * 8));
     }
   }
   if (tid == 0) descale[blk] = amax == 0.f ? 1.f : amax / kE4M3Max;

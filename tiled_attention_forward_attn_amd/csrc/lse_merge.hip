@@ -14,7 +14,8 @@
 // HBM-bound: a row reads R (4 d + 4) bytes and writes 2 d + 4. D/4 lanes own
 // a row, 4 consecutive columns each (16-byte loads, 8-byte bf16 stores), so a
 // wave reads whole 256..1024-byte rows of one partial at a time; the loop
-// over partials is unrolled so several of those loads are in flight.
+// over partials is unrolled so several of those loads are in flight. Every
+// byte is read or written once, so the accesses carry the nontemporal hint.
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -43,7 +44,7 @@ void lse_merge_kernel(const float* __restrict__ op, const float* __restrict__ lp
     for (int r = 0; r < R; ++r) {
       const long long pr = (long long)r * rows + row;
       const float w = expf(lp[pr] - m);          // 0 for an empty partial
-      const f32x4 x = *(const f32x4*)(op + pr * D + c);
+      const f32x4 x = __builtin_nontemporal_load((const f32x4*)(op + pr * D + c));
       total += w;
       acc += w * x;
     }
@@ -52,7 +53,7 @@ void lse_merge_kernel(const float* __restrict__ op, const float* __restrict__ lp
   bf16x4 y;
 #pragma unroll
   for (int e = 0; e < 4; ++e) y[e] = (__bf16)(acc[e] * inv);
-  *(bf16x4*)(o + row * D + c) = y;
+  __builtin_nontemporal_store(y, (bf16x4*)(o + row * D + c));
   if (c == 0) lse[row] = total > 0.f ? m + logf(total) : -INFINITY;
 }
 
