@@ -52,11 +52,19 @@ struct DecodeWave {
   float c;
   i32x4 kres, vres;
   int koff[LOADS], voff[LOADS];
-  // paged cache: pool base, this sequence's block table row and this head
+  // paged cache: pool base, this sequence's block table row (read through the
+  // constant address space, so a scalar load that the copies' vmcnt waits do
+  // not drain) and this head; page_next is the page of the next tile to issue,
+  // read one tile ahead
   const uint16_t* kpool;
   const uint16_t* vpool;
-  const int* table;
-  int head, H, page_shift, num_pages;
+  const __attribute__((address_space(4))) int* table;
+  int head, H, page_shift, num_pages, page_next;
+
+  __device__ __forceinline__ int load_page(int t) const {
+    const int p0 = t * BN;
+    return p0 < k_hi ? table[p0 >> page_shift] : -1;
+  }
   bf16x8 qf[KSTEPS];
   f32x16 oacc[DBLK];
   f32x16 sacc[NKB];
@@ -72,8 +80,9 @@ struct DecodeWave {
       uint32_t bytes = 0;
       const uint16_t* kb = kpool;
       const uint16_t* vb = vpool;
+      const int page = page_next;   // tile t's page (-1 past the chunk)
+      page_next = load_page(t + 1);
       if (p0 < k_hi) {
-        const int page = __builtin_amdgcn_readfirstlane(table[p0 >> page_shift]);
         if ((unsigned)page < (unsigned)num_pages) {
           const size_t row = ((size_t)page * H + head) * ((size_t)1 << page_shift) +
                              (p0 & ((1 << page_shift) - 1));
@@ -209,7 +218,7 @@ void attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     st.H = pc.H;
     st.page_shift = pc.page_shift;
     st.num_pages = pc.num_pages;
-    st.table = pc.block_table + (size_t)b * pc.max_pages;
+    st.table = (const __attribute__((address_space(4))) int*)(pc.block_table + (size_t)b * pc.max_pages);
     st.kpool = K;
     st.vpool = V;
     const int len = __builtin_amdgcn_readfirstlane(pc.seq_lens[b]);
@@ -254,6 +263,7 @@ void attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       st.voff[u] = (row * D + (pc ^ bf16_swz_v<D>(row)) * 8) * 2;
     }
     const int t0 = k_lo / BN, t1 = (st.k_hi + BN - 1) / BN;
+    if constexpr (PAGED) st.page_next = st.load_page(t0);
     st.template issue<0>(t0);
     int t = t0;
     for (; t + 1 < t1; t += 2) {
