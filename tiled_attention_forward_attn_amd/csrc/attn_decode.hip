@@ -97,8 +97,8 @@ struct DecodeWave {
     }
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      copy_to_lds16<true>(kres, kl[ST] + u * 1024, koff[u], soff);
-      copy_to_lds16<true>(vres, vl[ST] + u * 1024, voff[u], soff);
+      copy_to_lds16(kres, kl[ST] + u * 1024, koff[u], soff);
+      copy_to_lds16(vres, vl[ST] + u * 1024, voff[u], soff);
     }
   }
 

@@ -50,21 +50,12 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // (The compiler cannot tell that the transposing LDS reads of one tile never
 // touch the tile still being copied, and would otherwise wait for every copy
 // in flight before each of them.) M0 carries the LDS address.
-// NT: nontemporal hint, for data that is read exactly once (decode's cache
-// stream); the prefill kernels re-read K and V from L2 and leave it off.
-template <bool NT = false>
 __device__ __forceinline__ void copy_to_lds16(i32x4 rsrc, const lds_char* lds_base, int voffset,
                                               int soffset) {
-  if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds nt"
-                 :
-                 : "s"((uint32_t)(uintptr_t)lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"((uint32_t)(uintptr_t)lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
-                 : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"((uint32_t)(uintptr_t)lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N of this wave's vector-memory loads are outstanding.
