@@ -21,7 +21,7 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kBM = 128;      // query rows per workgroup, 32 per wave
+constexpr int kBM = 128;      // query rows of a 4-wave workgroup, 32 per wave
 constexpr int kBN = 64;       // keys per K/V tile
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;

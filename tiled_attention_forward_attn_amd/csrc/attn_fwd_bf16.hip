@@ -1,8 +1,9 @@
 // Fused attention forward, bf16 inputs, for gfx950 (MI355X / CDNA4).
 //
-// A workgroup of 4 waves owns QB x 128 queries of one (batch, head): each
-// wave owns QB blocks of 32 queries. It streams the allowed key/value tiles
-// (BN keys each) through LDS. Scores, probabilities and the output
+// A workgroup of NW waves (4, or 8 for large unwindowed grids at d = 128)
+// owns NW x 32 x QB queries of one (batch, head): each wave owns QB blocks of
+// 32 queries. It streams the allowed key/value tiles (BN keys each) through
+// LDS. Scores, probabilities and the output
 // accumulator never leave registers; the N x N score matrix is never formed.
 // This is the tiled, fused scheme of [WGC] sections 1-2 (QK^T -> softmax
 // statistics -> PV with running max/sum and output rescale) and [YT] sections
