@@ -136,12 +136,13 @@ def check_workload_heads(o, lse, w, heads, rows_per_head):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N,causal,window", [(300, False, -1), (300, True, -1), (257, True, 40),
-                                             (512, False, 100), (260, True, 255), (513, True, -1)])
+@pytest.mark.parametrize("N,causal,window", [(300, False, -1), (513, False, -1), (300, True, -1),
+                                             (257, True, 40), (512, False, 100), (260, True, 255),
+                                             (513, True, -1)])
 def test_bf16_wide_grid(lib, d, N, causal, window):
-    # B * H * ceil(N / 256) >= 1024: at d = 128 without a window this selects
-    # the 8-wave workgroups (256 queries each); ragged N and every mask kind,
-    # compared on sampled heads
+    # B * H * ceil(N / 256) >= 1024: at d = 128 without a mask this selects
+    # the 8-wave workgroups (256 queries each); ragged N, and the masked cases
+    # of the same large grid, compared on sampled heads
     B, H = 32, 32
     q, k, v = make_qkv(B, H, N, d, seed=N + d + window)
     o, lse = lib.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, window=window)

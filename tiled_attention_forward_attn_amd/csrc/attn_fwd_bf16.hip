@@ -426,10 +426,11 @@ constexpr int kQB256 = 1, kBN256 = 32;
 
 // Waves per workgroup at d = 128 (two waves per SIMD either way): one 8-wave
 // workgroup per CU copies each K/V tile into LDS once for 256 queries, half
-// the L2 -> LDS traffic and LDS writes of two 4-wave workgroups. Used without
-// a sliding window (a band cuts mask edges through more key tiles of a
-// 256-query tile) and when there are at least this many 256-query tiles, so
-// that the grid still fills the CUs and balances.
+// the L2 -> LDS traffic and LDS writes of two 4-wave workgroups. Used for
+// unmasked problems only (with a causal or window mask, the uneven work per
+// query tile balances worse over half as many, twice as large tiles) and when
+// there are at least this many 256-query tiles, so that the grid still fills
+// the CUs.
 constexpr long long kWideGridMin = 1024;
 
 template <int D, int BN, int QB, int NW>
@@ -446,7 +447,8 @@ void launch_cfg(const FwdArgs& a, float c, int qsign, hipStream_t stream) {
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   const float c = fabsf(a.scale) * kLog2e;  // |scale| * log2(e)
   const int qsign = a.scale < 0.f ? (int)0x80008000u : 0;
-  const bool wide = a.window < 0 && (long long)((a.N + 255) / 256) * a.BH >= kWideGridMin;
+  const bool wide = !a.causal && a.window < 0 &&
+                    (long long)((a.N + 255) / 256) * a.BH >= kWideGridMin;
   if (a.d == 128) {
     if (wide) launch_cfg<128, kBN128, kQB128, 8>(a, c, qsign, stream);
     else launch_cfg<128, kBN128, kQB128, 4>(a, c, qsign, stream);
