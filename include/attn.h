@@ -66,6 +66,8 @@ enum {
  * inside the 32-bit byte range of the buffer descriptors the kernels read
  * through ((2^23 + 64) * 128 * 2 < 2^32). */
 #define ATTN_MAX_N (1 << 23)
+/* The same bound at d = 256, where a row is twice as long. */
+#define ATTN_MAX_N_D256 (1 << 22)
 #define ATTN_MAX_BH (1 << 24)
 /* Rows per fp8 scaling block, for Q, K and V alike. */
 #define ATTN_FP8_BLOCK_ROWS 128
@@ -89,7 +91,8 @@ enum {
  *   lse       [B][H][N] fp32 output, may NOT be NULL.
  *   B, H, N   batch, heads, sequence length (queries = keys = N).
  *   d         head dimension: 64 or 128 ([WGC] "适用场景"); 256 with dtype 0
- *             ([WGC] "后续方向" lists it as the next step).
+ *             ([WGC] "后续方向" lists it as the next step), with
+ *             N <= ATTN_MAX_N_D256.
  *   causal    1: key j allowed only if j <= i. 0: no causal cut.
  *   window    -1: no window. w >= 0: keys with i - w <= j <= i (causal) or
  *             |i - j| <= w (non-causal): the band of [YT] section 2.1.2, both

@@ -78,6 +78,7 @@ E = header_codes()
     (dict(d=96), "ATTN_E_HEADDIM"), (dict(d=512), "ATTN_E_HEADDIM"), (dict(d=0), "ATTN_E_HEADDIM"),
     (dict(d=256, dtype=1, dq=A + 5 * GAP, dk=A + 6 * GAP, dv=A + 7 * GAP), "ATTN_E_HEADDIM"),
     (dict(d=256, dtype=2, dv=A + 7 * GAP), "ATTN_E_HEADDIM"),
+    (dict(d=256, N=(1 << 22) + 1, B=1, H=1), "ATTN_E_SHAPE"),  # 32-bit descriptor range at d = 256
     (dict(dtype=3), "ATTN_E_DTYPE"), (dict(dtype=-1), "ATTN_E_DTYPE"),
     (dict(q=None), "ATTN_E_NULL"), (dict(k=None), "ATTN_E_NULL"), (dict(v=None), "ATTN_E_NULL"),
     (dict(o=None), "ATTN_E_NULL"), (dict(lse=None), "ATTN_E_NULL"),

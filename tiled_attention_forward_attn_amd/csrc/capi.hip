@@ -29,6 +29,7 @@ int check_shape(int B, int H, int N, int d, bool d256, bool* empty) {
   if (*empty) return ATTN_OK;
   if (N > ATTN_MAX_N || (long long)B * H > ATTN_MAX_BH) return ATTN_E_SHAPE;
   if (d != 64 && d != 128 && !(d256 && d == 256)) return ATTN_E_HEADDIM;
+  if (d == 256 && N > ATTN_MAX_N_D256) return ATTN_E_SHAPE;
   // one workgroup per 128-row block of every head must fit the 1-D grid
   if ((long long)((N + 127) / 128) * B * H > kMaxGrid) return ATTN_E_SHAPE;
   return ATTN_OK;
