@@ -155,6 +155,24 @@ def test_bf16_wide_grid(lib, d, N, causal, window):
         check_bf16(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ref_o, ref_lse, f"head {(b, h)}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [3900, 4096, 4097])
+def test_bf16_causal_tile_pairs(lib, d, N):
+    # Causal problems of up to 32 query tiles of 128 per head run the tiles
+    # p and nqt-1-p in one workgroup: N = 3900 (31 tiles, a lone middle
+    # tile), 4096 (32 tiles, the largest paired case) and 4097 (33 tiles, one
+    # tile per workgroup). Sampled rows, including each tile's first and last.
+    B, H = 2, 3
+    q, k, v = make_qkv(B, H, N, d, seed=N + d)
+    o, lse = lib.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rows = sorted(set(list(range(0, N, 128)) + list(range(127, N, 128)) + list(range(45, N, 97)) + [N - 1]))
+    for b, h in ((0, 0), (1, 2)):
+        ref_o, ref_lse = attention_rows(q[b, h], k[b, h], v[b, h], 1 / math.sqrt(d), True, -1, rows)
+        check_bf16(o[b, h, rows], lse[b, h, rows], ref_o, ref_lse, f"head {(b, h)}")
+
+
 @pytest.mark.parametrize("name", ["noncausal_b1h2n256d64_bf16", "causal_b4h16n2048d128_bf16"])
 def test_workload_full_compare(lib, name):
     w = BY_NAME[name]

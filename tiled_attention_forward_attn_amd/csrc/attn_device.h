@@ -154,14 +154,12 @@ struct TileRange {
   int bh, q0, q_last, kt0, kt1;
 };
 
-// Masked problems (causal or windowed) visit their heaviest query tiles first.
-// bm: query rows per workgroup, bn: keys per key tile.
-__device__ __forceinline__ TileRange tile_range(int N, int nqt, int causal, int window,
-                                                int bm = kBM, int bn = kBN) {
+// Query tile qt of (batch*head) bh. bm: query rows per workgroup, bn: keys
+// per key tile.
+__device__ __forceinline__ TileRange tile_range_at(int bh, int qt, int N, int causal, int window,
+                                                   int bm, int bn) {
   TileRange t;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  t.bh = logical / nqt;
-  const int qt = (causal || window >= 0) ? nqt - 1 - logical % nqt : logical % nqt;
+  t.bh = bh;
   t.q0 = qt * bm;
   t.q_last = min(N, t.q0 + bm) - 1;
   // allowed keys of the whole query tile: [k_lo, k_hi)
@@ -171,6 +169,75 @@ __device__ __forceinline__ TileRange tile_range(int N, int nqt, int causal, int 
   t.kt1 = (k_hi + bn - 1) / bn;
   return t;
 }
+
+// One query tile per workgroup; masked problems (causal or windowed) visit
+// their heaviest query tiles first.
+__device__ __forceinline__ TileRange tile_range(int N, int nqt, int causal, int window,
+                                                int bm = kBM, int bn = kBN) {
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = (causal || window >= 0) ? nqt - 1 - logical % nqt : logical % nqt;
+  return tile_range_at(logical / nqt, qt, N, causal, window, bm, bn);
+}
+
+// Causal pairing: workgroup u takes the query tiles nqt-1-p and p of one head
+// (p = u mod ceil(nqt/2); one tile when they coincide), heavier first. Under
+// a causal mask their key-tile counts add up to the same total for every p,
+// so every workgroup carries the same work and no short workgroups are left
+// for the end of the grid.
+struct TilePair {
+  int bh, first, second;   // second < 0: a single tile
+};
+__device__ __forceinline__ TilePair tile_pair(int nqt) {
+  const int npair = (nqt + 1) >> 1;
+  const int u = xcd_remap(blockIdx.x, gridDim.x);
+  TilePair t;
+  t.bh = u / npair;
+  const int p = u % npair;
+  t.first = nqt - 1 - p;
+  t.second = p != t.first ? p : -1;
+  return t;
+}
+
+// Wave-uniform values that are needed only between query tiles (base
+// pointers) are parked in VGPRs, so that the SGPRs stay free for the tile
+// loop: the empty asm hides the value from the compiler's
+// uniformity analysis, so it is held per lane; uniform() reads it back into
+// an SGPR where it is used. The asm is re-issued at every use so that the
+// read-back cannot be hoisted out of the loop.
+__device__ __forceinline__ int park(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ int uniform(int parked) {
+  return __builtin_amdgcn_readfirstlane(park(parked));
+}
+// A pointer, parked when P (else held as is).
+template <bool P>
+struct ParkedPtr {
+  int lo, hi;
+  __device__ __forceinline__ explicit ParkedPtr(const void* p) {
+    const unsigned long long a = (unsigned long long)p;
+    lo = (int)(uint32_t)a;
+    hi = (int)(uint32_t)(a >> 32);
+    if constexpr (P) {
+      lo = park(lo);
+      hi = park(hi);
+    }
+  }
+  // wave-uniform read-back
+  template <class T>
+  __device__ __forceinline__ T* get() const {
+    if constexpr (P)
+      return (T*)(((unsigned long long)(uint32_t)uniform(hi) << 32) | (uint32_t)uniform(lo));
+    else
+      return (T*)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+  }
+  // per-lane read-back (for per-lane addresses)
+  template <class T>
+  __device__ __forceinline__ T* lanes() const {
+    return (T*)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+  }
+};
 
 // Key tiles [ia, ib) inside [kt0, kt1) are "interior": every key of the tile is
 // allowed for every query of the query tile, so they need no element mask.

@@ -40,7 +40,10 @@
 //    visited ([YT] section 2.1.2); only tiles straddling the band's edge or the
 //    ragged end of the sequence carry mask code.
 //  * Workgroup ids are remapped so the query tiles of one head land on one XCD
-//    and share K/V in its L2; masked problems issue their heaviest tiles first.
+//    and share K/V in its L2; masked problems issue their heaviest tiles
+//    first. Short causal problems give each workgroup the tiles p and
+//    nqt-1-p of a head, so every workgroup carries the same work; the second
+//    tile's Q loads and first K copy overlap the first tile's drain.
 // The kernel state lives in one struct whose members are all force-inlined, so
 // every array is promoted to registers.
 #include "attn_device.h"
@@ -301,7 +304,9 @@ struct Bf16Fwd {
   }
 };
 
-template <int D, int BN, int QB, int NW>
+// PAIRED: each workgroup runs a causal tile pair (see TilePair); otherwise
+// one query tile per workgroup, heaviest first under a mask.
+template <int D, int BN, int QB, int NW, bool PAIRED>
 __global__ __launch_bounds__(64 * NW, (QB == 1 && D <= 128) ? 8 / NW : 1)
 void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
@@ -319,38 +324,19 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   st.kl[1] = (lds_char*)k1s;
   st.vl[0] = (lds_char*)v0s;
   st.vl[1] = (lds_char*)v1s;
-  const TileRange tr = tile_range(N, nqt, causal, window, BMQ, BN);
   st.N = N;
   st.causal = causal;
   st.window = window;
-  st.kt0 = tr.kt0;
-  st.kt1 = tr.kt1;
   st.c = c;
   const int tid = threadIdx.x;
   st.lane = tid & 63;
   st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   st.h = st.lane >> 5;
   st.l32 = st.lane & 31;
-#pragma unroll
-  for (int b = 0; b < QB; ++b) st.qrow[b] = tr.q0 + st.wave * 32 * QB + 32 * b + st.l32;
-  const size_t head = (size_t)tr.bh * N * D;
-
-  // Q fragments (B operand of S^T = K Q^T): lane holds q[qrow][16t + 8h .. +7].
-#pragma unroll
-  for (int b = 0; b < QB; ++b)
-#pragma unroll
-    for (int t = 0; t < S::KSTEPS; ++t) {
-      i32x4 x = {0, 0, 0, 0};
-      if (st.qrow[b] < N) x = *(const i32x4*)(Q + head + (size_t)st.qrow[b] * D + 16 * t + 8 * st.h);
-      x ^= qsign;  // exact sign flip for negative scales
-      st.qf[b][t] = __builtin_bit_cast(bf16x8, x);
-    }
 
   // HBM -> LDS copies. Chunk p of a tile's LDS image (16 B, p = 64 * block +
   // lane) sits at row p / DCH, physical column p % DCH, which holds logical
   // column (p % DCH) ^ swizzle(row); each lane fetches exactly that chunk.
-  st.kres = make_rsrc(K + head, (uint32_t)N * D * 2);
-  st.vres = make_rsrc(V + head, (uint32_t)N * D * 2);
 #pragma unroll
   for (int u = 0; u < S::LOADS; ++u) {
     const int p = (u * NW + st.wave) * 64 + st.lane;
@@ -359,60 +345,125 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     st.voff[u] = (row * D + (pc ^ bf16_swz_v<D>(row)) * 8) * 2;
   }
 
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-#pragma unroll
-    for (int db = 0; db < S::DBLK; ++db) st.oacc[b][db] = f32x16{};
-    st.m[b] = -INFINITY;   // reference max of c * s (base-2 units)
-    st.l[b] = 0.f;         // running sum over this lane's keys
-    st.alpha[b] = 1.f;
-  }
-  st.owe_rescale = false;
+  // Base pointers are parked (see park) while the tiles run.
+  const ParkedPtr<PAIRED> pq(Q), pk(K), pv(V), po(O), plse(LSE);
 
-  const int kt0 = tr.kt0, kt1 = tr.kt1;
-  if (kt0 < kt1) {
-    st.template issue_k<0>(kt0);
-    const InteriorSpan span = interior_span(tr, N, causal, window, BN);
-    // the first tile has no PV yet
-    if (kt0 < span.ia || kt0 >= span.ib) st.template iteration<true, 0, true>(kt0);
-    else st.template iteration<false, 0, true>(kt0);
-    const int a = min(max(span.ia, kt0 + 1), kt1), b = min(max(span.ib, a), kt1);
-    st.template run<true>(kt0 + 1, a);
-    st.template run<false>(a, b);
-    st.template run<true>(b, kt1);
-    // drain: PV of the last tile
-    st.sync_tiles();
-    st.rescale();
-    if ((kt1 - 1 - kt0) & 1) {
-      st.template read_v<1>();
-      st.template pv<1>();
-    } else {
-      st.template read_v<0>();
-      st.template pv<0>();
+  // Query tile set-up: key-tile range, query rows, this head's K/V buffer
+  // descriptors, the Q fragments (B operand of S^T = K Q^T: lane holds
+  // q[qrow][16t + 8h .. +7]) and the copy of the first K tile into stage 0.
+  // Called for a pair's second tile while the first one drains, so the Q
+  // loads and the first copy are in flight during its last PV and epilogue.
+  auto begin = [&](const TileRange& tr) __attribute__((always_inline)) {
+    st.kt0 = tr.kt0;
+    st.kt1 = tr.kt1;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) st.qrow[b] = tr.q0 + st.wave * 32 * QB + 32 * b + st.l32;
+    const size_t head = (size_t)tr.bh * N * D;
+    const uint16_t* Qp = pq.template get<const uint16_t>();
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int t = 0; t < S::KSTEPS; ++t) {
+        i32x4 x = {0, 0, 0, 0};
+        if (st.qrow[b] < N) x = *(const i32x4*)(Qp + head + (size_t)st.qrow[b] * D + 16 * t + 8 * st.h);
+        x ^= qsign;  // exact sign flip for negative scales
+        st.qf[b][t] = __builtin_bit_cast(bf16x8, x);
+      }
+    st.kres = make_rsrc(pk.template get<const uint16_t>() + head, (uint32_t)N * D * 2);
+    st.vres = make_rsrc(pv.template get<const uint16_t>() + head, (uint32_t)N * D * 2);
+    if (tr.kt0 < tr.kt1) st.template issue_k<0>(tr.kt0);
+  };
+
+  TileRange tr;
+  TilePair pair = {0, 0, -1};
+  if constexpr (PAIRED) {
+    pair = tile_pair(nqt);
+    tr = tile_range_at(pair.bh, pair.first, N, causal, window, BMQ, BN);
+  } else {
+    tr = tile_range(N, nqt, causal, window, BMQ, BN);
+  }
+  begin(tr);
+
+  for (;;) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+#pragma unroll
+      for (int db = 0; db < S::DBLK; ++db) st.oacc[b][db] = f32x16{};
+      st.m[b] = -INFINITY;   // reference max of c * s (base-2 units)
+      st.l[b] = 0.f;         // running sum over this lane's keys
+      st.alpha[b] = 1.f;
     }
-  }
+    st.owe_rescale = false;
 
-  // ---- epilogue: O = O^T / l (bf16, RNE), LSE = ln 2 * (m + log2 l)
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    const float lt = halves_sum(st.l[b]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (st.qrow[b] < N) {
-      uint16_t* orow = O + head + (size_t)st.qrow[b] * D;
-#pragma unroll
-      for (int db = 0; db < S::DBLK; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          bf16x4 o4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(st.oacc[b][db][4 * g4 + e] * inv);
-          *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * st.h) = o4;
+    const int kt0 = tr.kt0, kt1 = tr.kt1;
+    const InteriorSpan span = interior_span(tr, N, causal, window, BN);
+    int cur_bh = tr.bh, cur_q0 = tr.q0;   // for the epilogue
+    if constexpr (PAIRED) {
+      cur_bh = park(cur_bh);
+      cur_q0 = park(cur_q0);
+    }
+    // A pair's second tile, if any, is set up while the first one drains.
+    auto advance = [&]() __attribute__((always_inline)) {
+      if constexpr (PAIRED) {
+        if (pair.second >= 0) {
+          tr = tile_range_at(pair.bh, pair.second, N, causal, window, BMQ, BN);
+          pair.second = -1;
+          begin(tr);
+          return true;
         }
-      if (st.h == 0) {
-        const float muse = st.m[b] == -INFINITY ? 0.f : st.m[b];
-        LSE[(size_t)tr.bh * N + st.qrow[b]] = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
+      }
+      return false;
+    };
+    bool more;
+    if (kt0 < kt1) {
+      // the first tile has no PV yet
+      if (kt0 < span.ia || kt0 >= span.ib) st.template iteration<true, 0, true>(kt0);
+      else st.template iteration<false, 0, true>(kt0);
+      const int a = min(max(span.ia, kt0 + 1), kt1), b = min(max(span.ib, a), kt1);
+      st.template run<true>(kt0 + 1, a);
+      st.template run<false>(a, b);
+      st.template run<true>(b, kt1);
+      // drain: PV of the last tile. After this barrier no wave reads either K
+      // stage again, so the next query tile's first K copy may start.
+      st.sync_tiles();
+      more = advance();
+      st.rescale();
+      if ((kt1 - 1 - kt0) & 1) {
+        st.template read_v<1>();
+        st.template pv<1>();
+      } else {
+        st.template read_v<0>();
+        st.template pv<0>();
+      }
+    } else {
+      more = advance();
+    }
+
+    // ---- epilogue: O = O^T / l (bf16, RNE), LSE = ln 2 * (m + log2 l)
+    const size_t head = (size_t)cur_bh * N * D;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int qrow = cur_q0 + st.wave * 32 * QB + 32 * b + st.l32;
+      const float lt = halves_sum(st.l[b]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if (qrow < N) {
+        uint16_t* orow = po.template lanes<uint16_t>() + head + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < S::DBLK; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            bf16x4 o4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(st.oacc[b][db][4 * g4 + e] * inv);
+            *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * st.h) = o4;
+          }
+        if (st.h == 0) {
+          const float muse = st.m[b] == -INFINITY ? 0.f : st.m[b];
+          plse.template lanes<float>()[(size_t)cur_bh * N + qrow] = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
+        }
       }
     }
+    if (!more) break;
   }
 }
 
@@ -433,13 +484,24 @@ constexpr int kQB256 = 1, kBN256 = 32;
 // the CUs.
 constexpr long long kWideGridMin = 1024;
 
-template <int D, int BN, int QB, int NW>
+// Causal problems of at most this many 128-query tiles per head run tile
+// pairs. Pairs halve the number of workgroups and give them equal work, which
+// pays where the tiles are short (nqt+1 key-tile rows per pair). With more
+// tiles, the second tiles of the pairs start out of step and lose the shared
+// K/V stream in L2, while the heaviest-first order already balances the
+// grid. Windowed tiles carry near-equal work, so pairing buys nothing there.
+constexpr int kPairMaxTiles = 32;
+
+// One workgroup per tile pair (PAIRED) or per query tile.
+template <int D, int BN, int QB, int NW, bool PAIRED>
 void launch_cfg(const FwdArgs& a, float c, int qsign, hipStream_t stream) {
   const int rows = 32 * NW * QB;
   const int nqt = (a.N + rows - 1) / rows;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BN, QB, NW>), dim3(nqt * a.BH), dim3(64 * NW), 0,
-                     stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.N, nqt, c, a.causal, a.window, qsign);
+  const int per_head = PAIRED ? (nqt + 1) / 2 : nqt;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BN, QB, NW, PAIRED>), dim3(per_head * a.BH),
+                     dim3(64 * NW), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.N, nqt, c, a.causal, a.window,
+                     qsign);
 }
 
 }  // namespace
@@ -449,13 +511,16 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   const int qsign = a.scale < 0.f ? (int)0x80008000u : 0;
   const bool wide = !a.causal && a.window < 0 &&
                     (long long)((a.N + 255) / 256) * a.BH >= kWideGridMin;
+  const bool pair = a.causal && a.window < 0 && (a.N + 127) / 128 <= kPairMaxTiles;
   if (a.d == 128) {
-    if (wide) launch_cfg<128, kBN128, kQB128, 8>(a, c, qsign, stream);
-    else launch_cfg<128, kBN128, kQB128, 4>(a, c, qsign, stream);
+    if (wide) launch_cfg<128, kBN128, kQB128, 8, false>(a, c, qsign, stream);
+    else if (pair) launch_cfg<128, kBN128, kQB128, 4, true>(a, c, qsign, stream);
+    else launch_cfg<128, kBN128, kQB128, 4, false>(a, c, qsign, stream);
   } else if (a.d == 256) {
-    launch_cfg<256, kBN256, kQB256, 4>(a, c, qsign, stream);
+    launch_cfg<256, kBN256, kQB256, 4, false>(a, c, qsign, stream);
   } else {
-    launch_cfg<64, kBN64, kQB64, 4>(a, c, qsign, stream);
+    if (pair) launch_cfg<64, kBN64, kQB64, 4, true>(a, c, qsign, stream);
+    else launch_cfg<64, kBN64, kQB64, 4, false>(a, c, qsign, stream);
   }
   return hipGetLastError();
 }
