@@ -170,12 +170,14 @@ __device__ __forceinline__ TileRange tile_range_at(int bh, int qt, int N, int ca
   return t;
 }
 
-// One query tile per workgroup; masked problems (causal or windowed) visit
-// their heaviest query tiles first.
+// One query tile per workgroup. Within a head, causal problems visit their
+// heaviest (last) query tiles first. All others go in ascending order: under
+// a band, the first key tiles of a query tile are the last ones of the tile
+// before it, so a new workgroup finds them in L2.
 __device__ __forceinline__ TileRange tile_range(int N, int nqt, int causal, int window,
                                                 int bm = kBM, int bn = kBN) {
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = (causal || window >= 0) ? nqt - 1 - logical % nqt : logical % nqt;
+  const int qt = (causal && window < 0) ? nqt - 1 - logical % nqt : logical % nqt;
   return tile_range_at(logical / nqt, qt, N, causal, window, bm, bn);
 }
 

@@ -40,10 +40,12 @@
 //    visited ([YT] section 2.1.2); only tiles straddling the band's edge or the
 //    ragged end of the sequence carry mask code.
 //  * Workgroup ids are remapped so the query tiles of one head land on one XCD
-//    and share K/V in its L2; masked problems issue their heaviest tiles
-//    first. Short causal problems give each workgroup the tiles p and
-//    nqt-1-p of a head, so every workgroup carries the same work; the second
-//    tile's Q loads and first K copy overlap the first tile's drain.
+//    and share K/V in its L2. Causal problems issue their heaviest tiles
+//    first; banded ones go in ascending order, so a tile's first key tiles
+//    are still in L2 from the tile before. Short causal problems give each
+//    workgroup the tiles p and nqt-1-p of a head, so every workgroup carries
+//    the same work; the second tile's Q loads and first K copy overlap the
+//    first tile's drain.
 // The kernel state lives in one struct whose members are all force-inlined, so
 // every array is promoted to registers.
 #include "attn_device.h"
@@ -165,30 +167,41 @@ struct Bf16Fwd {
   }
 
   // Disallowed keys of an edge tile get score -inf. sacc[b][kb][i] is the
-  // score of key k0 + 32 kb + 8 (i/4) + 4 h + i%4 against query qrow[b].
+  // score of key base + 32 kb + 8 (i/4) + i%4 (base = k0 + 4 h) against query
+  // qrow[b]. The allowed keys of a query form one range [lo, hi] (key_allowed:
+  // below N, causal or band upper edge, band lower edge), so each lane
+  // computes that range once per tile and each element needs two compares
+  // against a constant offset.
   __device__ __forceinline__ void mask(int kt) {
-    const int k0 = kt * BN;
+    const int base = kt * BN + 4 * h;
+    const int w = min(window, N);   // a band wider than N cuts nothing
 #pragma unroll
-    for (int b = 0; b < QB; ++b)
+    for (int b = 0; b < QB; ++b) {
+      int hi = N - 1;
+      if (causal) hi = min(hi, qrow[b]);
+      else if (window >= 0) hi = min(hi, qrow[b] + w);
+      const int lo = window >= 0 ? qrow[b] - w : 0;
+      const int ohi = hi - base, olo = lo - base;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (!key_allowed(key, qrow[b], N, causal, window)) sacc[b][kb][i] = -INFINITY;
+          const int off = kb * 32 + 8 * (i >> 2) + (i & 3);
+          if (off > ohi || off < olo) sacc[b][kb][i] = -INFINITY;
         }
+    }
   }
 
-  // P set PB of query block b = bf16(2^(c s - muse)) (masked keys 0); returns
-  // this lane's sum of the rounded values (the ones PV multiplies).
-  template <bool EDGE, int PB>
+  // P set PB of query block b = bf16(2^(c s - muse)); returns this lane's sum
+  // of the rounded values (the ones PV multiplies). c > 0 always (a zero
+  // scale zeroes Q instead), so a masked key's -inf score gives p = 0.
+  template <int PB>
   __device__ __forceinline__ float exponentiate(int b, float muse) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(sacc[b][kb][i], c, -muse));
-        if constexpr (EDGE) p = sacc[b][kb][i] == -INFINITY ? 0.f : p;
+        const float p = fast_exp2(fmaf(sacc[b][kb][i], c, -muse));
         pbuf[PB][b][kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
       }
     float part[PST];
@@ -216,8 +229,11 @@ struct Bf16Fwd {
       bool over = false;
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
-        rs[b] = exponentiate<EDGE, PB>(b, m[b]);
+        rs[b] = exponentiate<PB>(b, m[b]);
         over = over || !(rs[b] <= kFastLimit);
+        // A row that has seen no allowed key yet (m = -inf) gives -inf + inf
+        // for its masked keys here; it takes the exact step instead.
+        if constexpr (EDGE) over = over || m[b] == -INFINITY;
       }
       if (__ballot(over) == 0) {
 #pragma unroll
@@ -240,7 +256,7 @@ struct Bf16Fwd {
       const float mnew = grow ? mxs : m[b];
       const float muse = mnew == -INFINITY ? 0.f : mnew;
       const float a = fast_exp2(m[b] - muse);
-      const float rs = exponentiate<EDGE, PB>(b, muse);
+      const float rs = exponentiate<PB>(b, muse);
       l[b] = l[b] * a + rs;
       alpha[b] = a;
       m[b] = mnew;
@@ -305,13 +321,13 @@ struct Bf16Fwd {
 };
 
 // PAIRED: each workgroup runs a causal tile pair (see TilePair); otherwise
-// one query tile per workgroup, heaviest first under a mask.
+// one query tile per workgroup (order: see tile_range).
 template <int D, int BN, int QB, int NW, bool PAIRED>
 __global__ __launch_bounds__(64 * NW, (QB == 1 && D <= 128) ? 8 / NW : 1)
 void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                           float* __restrict__ LSE, int N, int nqt, float c, int causal,
-                          int window, int qsign) {
+                          int window, int qsign, int qkeep) {
   using S = Bf16Fwd<D, BN, QB, NW>;
   constexpr int BMQ = NW * 32 * QB;
   __shared__ __attribute__((aligned(1024))) char k0s[S::TILE];
@@ -366,7 +382,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       for (int t = 0; t < S::KSTEPS; ++t) {
         i32x4 x = {0, 0, 0, 0};
         if (st.qrow[b] < N) x = *(const i32x4*)(Qp + head + (size_t)st.qrow[b] * D + 16 * t + 8 * st.h);
-        x ^= qsign;  // exact sign flip for negative scales
+        x = (x & qkeep) ^ qsign;  // zero Q for a zero scale; exact sign flip for a negative one
         st.qf[b][t] = __builtin_bit_cast(bf16x8, x);
       }
     st.kres = make_rsrc(pk.template get<const uint16_t>() + head, (uint32_t)N * D * 2);
@@ -494,33 +510,36 @@ constexpr int kPairMaxTiles = 32;
 
 // One workgroup per tile pair (PAIRED) or per query tile.
 template <int D, int BN, int QB, int NW, bool PAIRED>
-void launch_cfg(const FwdArgs& a, float c, int qsign, hipStream_t stream) {
+void launch_cfg(const FwdArgs& a, float c, int qsign, int qkeep, hipStream_t stream) {
   const int rows = 32 * NW * QB;
   const int nqt = (a.N + rows - 1) / rows;
   const int per_head = PAIRED ? (nqt + 1) / 2 : nqt;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BN, QB, NW, PAIRED>), dim3(per_head * a.BH),
                      dim3(64 * NW), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.N, nqt, c, a.causal, a.window,
-                     qsign);
+                     qsign, qkeep);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  const float c = fabsf(a.scale) * kLog2e;  // |scale| * log2(e)
+  // c = |scale| log2(e) > 0. A zero scale zeroes Q instead (every score 0,
+  // exactly), so that a masked score of -inf times c stays -inf.
+  const float c = a.scale == 0.f ? 1.f : fabsf(a.scale) * kLog2e;
   const int qsign = a.scale < 0.f ? (int)0x80008000u : 0;
+  const int qkeep = a.scale == 0.f ? 0 : -1;
   const bool wide = !a.causal && a.window < 0 &&
                     (long long)((a.N + 255) / 256) * a.BH >= kWideGridMin;
   const bool pair = a.causal && a.window < 0 && (a.N + 127) / 128 <= kPairMaxTiles;
   if (a.d == 128) {
-    if (wide) launch_cfg<128, kBN128, kQB128, 8, false>(a, c, qsign, stream);
-    else if (pair) launch_cfg<128, kBN128, kQB128, 4, true>(a, c, qsign, stream);
-    else launch_cfg<128, kBN128, kQB128, 4, false>(a, c, qsign, stream);
+    if (wide) launch_cfg<128, kBN128, kQB128, 8, false>(a, c, qsign, qkeep, stream);
+    else if (pair) launch_cfg<128, kBN128, kQB128, 4, true>(a, c, qsign, qkeep, stream);
+    else launch_cfg<128, kBN128, kQB128, 4, false>(a, c, qsign, qkeep, stream);
   } else if (a.d == 256) {
-    launch_cfg<256, kBN256, kQB256, 4, false>(a, c, qsign, stream);
+    launch_cfg<256, kBN256, kQB256, 4, false>(a, c, qsign, qkeep, stream);
   } else {
-    if (pair) launch_cfg<64, kBN64, kQB64, 4, true>(a, c, qsign, stream);
-    else launch_cfg<64, kBN64, kQB64, 4, false>(a, c, qsign, stream);
+    if (pair) launch_cfg<64, kBN64, kQB64, 4, true>(a, c, qsign, qkeep, stream);
+    else launch_cfg<64, kBN64, kQB64, 4, false>(a, c, qsign, qkeep, stream);
   }
   return hipGetLastError();
 }
