@@ -10,17 +10,27 @@
 //  * a 128-row query tile is exactly one Q scaling block and a 64-key tile
 //    lies inside one K/V scaling block, so the score scale of a tile is the
 //    single number |scale| * log2(e) * dq * dk[block];
-//  * P is stored as E4M3(p * 2^8) with an exact running max, so p <= 1 and
-//    the row's largest probability is stored exactly (2^8); with the peaked
-//    softmax of outlier data that one weight is most of the output. The 2^8
-//    is folded into the exp argument; the row sum l is kept in fp32 from the
-//    unrounded p;
-//  * O is kept in units of the current V block's descale: the deferred
-//    rescale that the online softmax owes O also carries dv_old / dv_new
-//    when a tile starts a new V block, and the epilogue multiplies by the
-//    last one. (Folding dv_t / u into P instead would save that rescale but
-//    round the largest weight: measured 6x the kernel error on outlier data
-//    for a 4.5% speed gain.)
+//  * O is kept in units of u, the largest V descale of the workgroup's key
+//    range: tile t's V descale enters as rho_t = dv_t / u <= 1, folded into
+//    P, which is stored as E4M3(p * rho_t * 2^8) (2^8 and log2 rho_t are
+//    folded into the exp argument), so a new V block never rescales O;
+//  * the running max m of each row (log2 units) is kept as an integer, the
+//    ceiling of the exact running max, so p <= 1. Its growth is never
+//    applied to O by multiplication: O and l stay in units of a reference
+//    m_ref (the row's first finite m), and tile t's PV product is scaled by
+//    2^(m_t - m_ref) through the E8M0 B-operand scale of
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (one byte per lane, the lane's own
+//    query). Only when m_t - m_ref would exceed kMaxShift are O and l
+//    rebased, by an exact power of two. The online softmax of [WGC] section
+//    2 is unchanged in value: every tile's weights still relate to the
+//    running max; only where its rescale is applied moves;
+//  * the row sum l is the sum of the stored E4M3 weights, the values that
+//    multiply V, so the normalised weights add up to one and the rounding of
+//    the largest weight largely cancels. Each tile's sum is taken on the
+//    matrix core (one v_mfma_scale_f32_16x16x128_f8f6f4 of P^T, the PV B
+//    operand, against a constant 0/1 A operand chosen so that each lane
+//    receives the sum for the query it owns, see ones_operand), then added in
+//    fp32 with the factor 2^(m_t - m_ref) / rho_t.
 // A second instance (QBF) keeps Q and K in bf16 and computes S = Q K^T on the
 // bf16 matrix cores, with only V and P in E4M3: the score error that E4M3 Q
 // and K carry on data with large, aligned outlier channels (it grows with
@@ -38,7 +48,9 @@ namespace mi355attn {
 namespace {
 
 constexpr int kBN8 = 64;               // keys per tile (divides the 128-row scaling block)
-constexpr float kPScaleLog2 = 8.f;     // P is stored as E4M3(p * 2^8)
+constexpr float kPScaleLog2 = 8.f;     // P is stored as E4M3(p * rho * 2^8)
+constexpr float kMaxShift = 64.f;      // largest m - m_ref applied through the MFMA scale
+constexpr int kE8M0One = 127;          // E8M0 scale byte of 1.0
 
 // 16-byte chunk swizzles for E4M3 tiles (rows of D bytes): K is read 16 B per
 // lane from consecutive rows at one chunk; V is read by 16-lane groups as 8
@@ -56,6 +68,23 @@ __device__ __forceinline__ int swz_v8(int r) {
 // LDS row of key offset k within a tile: swap bits 2 and 3 (an involution).
 __device__ __forceinline__ int v8_row(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+// A operand of the row-sum MFMA. In v_mfma_*_16x16x128_f8f6f4 lane l holds
+// A row l % 16 over k chunk c = l / 16 (32 k values), and B column l % 16 over
+// the same chunk. Taking P's operand as B, chunk c of column n is the 32 keys
+// of lane n + 16c, i.e. query n + 16 (c % 2), key half c / 2. Row r of A is
+// one on the chunks with c % 2 == (r / 4) % 2 and zero elsewhere, so
+// D[r][n] = l(query n + 16 ((r / 4) % 2)). Lane l receives rows 4 (l / 16) ..
+// +3 of column l % 16: the sum of query l % 32, its own, in all four values.
+// Every byte of a lane's A operand holds the same value, and A and B are both
+// E4M3, so the pairing does not depend on how the instruction orders k within
+// a lane: byte b of A's lane r + 16c always meets byte b of B's lane n + 16c.
+// (An FP4 A operand would need half the registers, but its k order within a
+// lane is not the E4M3 one, and a lane-constant A then mixes the two queries.)
+__device__ __forceinline__ i32x8 ones_operand(int lane) {
+  const int one4 = ((lane >> 4) & 1) == ((lane >> 2) & 1) ? 0x38383838 : 0;  // 4 x E4M3 1.0
+  return i32x8{one4, one4, one4, one4, one4, one4, one4, one4};
 }
 
 __device__ __forceinline__ int cvt4(float a, float b, float c, float d) {
@@ -78,45 +107,56 @@ struct Fp8Fwd {
   static constexpr int VTILE = BN * D;                      // bytes of one V tile
   static constexpr int KLOADS = KTILE / (16 * kThreads);    // 16-byte copies per thread
   static constexpr int VLOADS = VTILE / (16 * kThreads);
+  // Copy round u of a tile lands kThreads / KDCH (or / VDCH) rows below round
+  // 0. Both swizzles depend on row bits 0..3 only and the V key order swaps
+  // bits 2 and 3, so round u's LDS offset is round 0's plus u * 16 * kThreads:
+  // one offset register per tensor, the rest in the scalar offset.
+  static_assert((kThreads / KDCH) % 16 == 0 && (kThreads / VDCH) % 16 == 0, "copy rounds");
 
   lds_char* kl[2];
   lds_char* vl[2];
   int N, causal, window, kt0, kt1, qrow;
   int lane, wave, h, l32;
   i32x4 kres, vres;
-  int koff[KLOADS], voff[VLOADS];
+  int koff, voff;     // LDS byte offset of this lane's copy in round 0
+  int krow, kswz;     // E4M3 K reads: l32 * D and swz_k8(l32) << 4
   const float* dk;
   const float* dv;
   float cq;
   // state
   QKFrag qf[KSTEPS];
   f32x16 oacc[DBLK];
+  float l;            // row sum, units of 2^(m_ref - 8) (both key halves)
+  i32x8 ones;
   f32x16 sacc[NKB];
   i32x8 pbuf[2];
   QKFrag kf[NKB][KSTEPS];
   i32x8 vf[DBLK];
-  float m, l;
-  float alpha;        // rescale owed by O before the next PV (incl. V unit change)
-  float v_unit;       // V descale whose units O is kept in
-  bool owe_rescale;
+  float m;           // running max (log2 units), an integer or -inf
+  float m_ref;       // units of O and l (log2), -inf until m is finite
+  float inv_u;       // 1 / u, u the largest V descale of the key range
+  int sb[2];         // E8M0 byte of 2^(m_t - m_ref) for P set 0 / 1
+  float lf[2];       // 2^(m_t - m_ref) / rho_t for P set 0 / 1
 
   template <int ST>
   __device__ __forceinline__ void issue_k(int kt) {
 #pragma unroll
     for (int u = 0; u < KLOADS; ++u)
-      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff[u], (int)((uint32_t)kt * KTILE));
+      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff,
+                    (int)((uint32_t)kt * KTILE + u * 16 * kThreads));
   }
   template <int ST>
   __device__ __forceinline__ void issue_v(int kt) {
 #pragma unroll
     for (int u = 0; u < VLOADS; ++u)
-      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff[u], (int)((uint32_t)kt * VTILE));
+      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff,
+                    (int)((uint32_t)kt * VTILE + u * 16 * kThreads));
   }
 
   // A operand of S^T = K Q^T for 32-key block kb. E4M3: lane holds
   // K8[32 kb + l32][64 t + 32 h .. +31]; bf16: K[32 kb + l32][16 t + 8 h .. +7].
   template <int ST>
-  __device__ __forceinline__ void read_k(int kb) {
+  __device__ __forceinline__ void read_k(int kb, const int (&ko)[KSTEPS][2]) {
     const lds_char* Ks = kl[ST];
     const int row = kb * 32 + l32;
 #pragma unroll
@@ -125,9 +165,8 @@ struct Fp8Fwd {
         const int ch = 2 * t + h;
         kf[kb][t] = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ bf16_swz_k<D>(row)) << 4));
       } else {
-        const int ch = 4 * t + 2 * h;
-        const i32x4 a0 = *(const lds_i32x4*)(Ks + row * D + ((ch ^ swz_k8<D>(row)) << 4));
-        const i32x4 a1 = *(const lds_i32x4*)(Ks + row * D + (((ch + 1) ^ swz_k8<D>(row)) << 4));
+        const i32x4 a0 = *(const lds_i32x4*)(Ks + kb * 32 * D + ko[t][0]);
+        const i32x4 a1 = *(const lds_i32x4*)(Ks + kb * 32 * D + ko[t][1]);
         kf[kb][t] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       }
     }
@@ -164,21 +203,31 @@ struct Fp8Fwd {
                                                                    0, 0, 0, 0);
     }
   }
-  // K fragments and S^T of the whole tile; bf16 K is read and multiplied one
-  // 32-key block at a time, so only one block of fragments is live.
+  // K fragments and S^T of the whole tile, read and multiplied one 32-key
+  // block at a time, so only one block of fragments is live.
+  // E4M3 K: lane reads chunks 4t + 2h and 4t + 2h + 1 of row 32 kb + l32.
+  // Rows 32 kb + l32 share the swizzle of l32 (it reads row bits 0..3), so
+  // block kb is a constant offset. The four chunk addresses are rebuilt every
+  // tile from two registers (one v_bitop3 each: krow has no bits where the
+  // chunk index sits) rather than kept live across the loop, where they would
+  // be spilled; the empty asm stops the compiler from hoisting them.
   template <int ST>
   __device__ __forceinline__ void read_k_qk() {
-    if constexpr (QBF) {
+    int ko[KSTEPS][2] = {};
+    if constexpr (!QBF) {
+      int sw = kswz;
+      asm volatile("" : "+v"(sw));
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        read_k<ST>(kb);
-        qk(kb);
+      for (int t = 0; t < KSTEPS; ++t) {
+        const int ch = 4 * t + 2 * h;
+        ko[t][0] = krow | ((ch << 4) ^ sw);
+        ko[t][1] = krow | (((ch + 1) << 4) ^ sw);
       }
-    } else {
+    }
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) read_k<ST>(kb);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) qk(kb);
+    for (int kb = 0; kb < NKB; ++kb) {
+      read_k<ST>(kb, ko);
+      qk(kb);
     }
   }
 
@@ -187,23 +236,36 @@ struct Fp8Fwd {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
       oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db], pbuf[PB], oacc[db], 0, 0, 0,
-                                                                 0, 0, 0);
+                                                                 kE8M0One, 0, sb[PB]);
+    const f32x4 rs =
+        __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pbuf[PB], f32x4{}, 0, 0, 0, 0, 0, 0);
+    l = fmaf(rs[0], lf[PB], l);
   }
 
-  // Online softmax of S(kt) into P set PB (E4M3 of p * 2^8; byte j of the
-  // operand is the key of sacc[j / 16][j % 16]).
+  // Online softmax of S(kt) into P set PB (E4M3 of p * rho * 2^8; byte j of
+  // the operand is the key of sacc[j / 16][j % 16]).
   template <bool EDGE, int PB>
   __device__ __forceinline__ void softmax(int kt) {
     const int k0 = kt * BN;
     const float c = QBF ? cq : cq * dk[k0 / 128];   // bf16 scores carry no descale
-    const float dv_t = dv[k0 / 128];
+    const float rho = dv[k0 / 128] * inv_u;          // <= 1
     if constexpr (EDGE) {
+      // sacc[kb][i] is key k0 + 4 h + 32 kb + 8 (i / 4) + i % 4. The allowed
+      // keys of a query (key_allowed) are one range [lo, hi], computed once
+      // per lane; each element then needs two compares against a constant.
+      const int base = k0 + 4 * h;
+      const int w = min(window, N);   // a band wider than N cuts nothing
+      int hi = N - 1;
+      if (causal) hi = min(hi, qrow);
+      else if (window >= 0) hi = min(hi, qrow + w);
+      const int lo = window >= 0 ? qrow - w : 0;
+      const int ohi = hi - base, olo = lo - base;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (!key_allowed(key, qrow, N, causal, window)) sacc[kb][i] = -INFINITY;
+          const int off = kb * 32 + 8 * (i >> 2) + (i & 3);
+          if (off > ohi || off < olo) sacc[kb][i] = -INFINITY;
         }
     }
     float sv[16 * NKB];
@@ -213,11 +275,24 @@ struct Fp8Fwd {
       for (int i = 0; i < 16; ++i) sv[16 * kb + i] = sacc[kb][i];
     float mx = halves_max(tree_max<16 * NKB>(sv));
     const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
-    const float mnew = max2(m, mxs);
+    const float mnew = max2(m, ceilf(mxs));
     const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float a = fast_exp2(m - muse);
-    // stored value p * 2^8 = 2^(c s - (muse - 8))
-    const float bias = muse - kPScaleLog2;
+    m_ref = m_ref == -INFINITY ? mnew : m_ref;
+    float shift = mnew == -INFINITY ? 0.f : mnew - m_ref;   // integer >= 0
+    if (__ballot(shift > kMaxShift) != 0) {
+      // rare: rebase O and l (all tiles so far: PV of the previous tile is
+      // ordered before this) by an exact power of two
+      const float f = shift > kMaxShift ? __builtin_ldexpf(1.f, -(int)shift) : 1.f;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) oacc[db] *= f;
+      l *= f;
+      m_ref = shift > kMaxShift ? mnew : m_ref;
+      shift = shift > kMaxShift ? 0.f : shift;
+    }
+    sb[PB] = kE8M0One + (int)shift;
+    lf[PB] = __builtin_ldexpf(__builtin_amdgcn_rcpf(rho), (int)shift);
+    // stored value p * rho * 2^8 = 2^(c s - (muse - 8 - log2 rho))
+    const float bias = muse - kPScaleLog2 - __builtin_amdgcn_logf(rho);
     float ps[16 * NKB];
 #pragma unroll
     for (int e = 0; e < 16 * NKB; ++e) {
@@ -227,26 +302,7 @@ struct Fp8Fwd {
 #pragma unroll
     for (int w = 0; w < 8; ++w)
       pbuf[PB][w] = cvt4(ps[4 * w], ps[4 * w + 1], ps[4 * w + 2], ps[4 * w + 3]);
-    // row sum of the unrounded p, as a tree, back in units of p
-    float part[8];
-#pragma unroll
-    for (int w = 0; w < 8; ++w) part[w] = (ps[4 * w] + ps[4 * w + 1]) + (ps[4 * w + 2] + ps[4 * w + 3]);
-    const float rs = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-    l = l * a + rs * fast_exp2(-kPScaleLog2);
     m = mnew;
-    // O (units of v_unit) must become a * O in units of dv_t before PV(kt);
-    // the unit ratio is exactly 1 inside one V block (v_rcp_f32: 1 ulp)
-    const float ratio = dv_t == v_unit ? 1.f : v_unit * __builtin_amdgcn_rcpf(dv_t);
-    alpha = a * ratio;
-    v_unit = dv_t;
-    owe_rescale = __ballot(alpha != 1.f) != 0;
-  }
-
-  __device__ __forceinline__ void rescale() {
-    if (owe_rescale) {
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
-    }
   }
 
   __device__ __forceinline__ void sync_tiles() {
@@ -262,7 +318,6 @@ struct Fp8Fwd {
     issue_v<PB>(j);
     if constexpr (!FIRST) read_v<PB ^ 1>();
     read_k_qk<PB>();
-    rescale();
     if constexpr (!FIRST) pv<PB ^ 1>();
     softmax<EDGE, PB>(j);
     __builtin_amdgcn_iglp_opt(0);
@@ -314,6 +369,8 @@ void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ K
   st.h = st.lane >> 5;
   st.l32 = st.lane & 31;
   st.qrow = tr.q0 + st.wave * 32 + st.l32;
+  st.krow = st.l32 * D;
+  st.kswz = swz_k8<D>(st.l32) << 4;
   const size_t head = (size_t)tr.bh * N * D;
   const int nsb = (N + 127) / 128;             // scaling blocks per head
   st.dk = QBF ? nullptr : DK + (size_t)tr.bh * nsb;
@@ -352,29 +409,39 @@ void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ K
   // (p % KDCH) ^ swizzle(row). The V image's LDS row r holds key v8_row(r).
   st.kres = make_rsrc((const char*)Kv + head * S::KBYTES, (uint32_t)N * D * S::KBYTES);
   st.vres = make_rsrc(V + head, (uint32_t)N * D);
-#pragma unroll
-  for (int u = 0; u < S::KLOADS; ++u) {
-    const int p = (u * 4 + st.wave) * 64 + st.lane;
+  {
+    const int p = st.wave * 64 + st.lane;        // chunk of copy round 0
     const int row = p / S::KDCH, pc = p % S::KDCH;
-    if constexpr (QBF) st.koff[u] = row * D * 2 + (pc ^ bf16_swz_k<D>(row)) * 16;
-    else st.koff[u] = row * D + (pc ^ swz_k8<D>(row)) * 16;
-  }
-#pragma unroll
-  for (int u = 0; u < S::VLOADS; ++u) {
-    const int p = (u * 4 + st.wave) * 64 + st.lane;
-    const int row = p / S::VDCH, pc = p % S::VDCH;
-    st.voff[u] = v8_row(row) * D + (pc ^ swz_v8<D>(row)) * 16;
+    if constexpr (QBF) st.koff = row * D * 2 + (pc ^ bf16_swz_k<D>(row)) * 16;
+    else st.koff = row * D + (pc ^ swz_k8<D>(row)) * 16;
+    const int vrow = p / S::VDCH, vpc = p % S::VDCH;
+    st.voff = v8_row(vrow) * D + (vpc ^ swz_v8<D>(vrow)) * 16;
   }
 
 #pragma unroll
   for (int db = 0; db < S::DBLK; ++db) st.oacc[db] = f32x16{};
-  st.m = -INFINITY;
   st.l = 0.f;
-  st.alpha = 1.f;
-  st.owe_rescale = false;
+  st.ones = ones_operand(st.lane);
+  st.m = -INFINITY;
+  st.m_ref = -INFINITY;
+  st.sb[0] = st.sb[1] = kE8M0One;
+  st.lf[0] = st.lf[1] = 0.f;
 
   const int kt0 = tr.kt0, kt1 = tr.kt1;
-  st.v_unit = kt0 < kt1 ? st.dv[kt0 * S::BN / 128] : 1.f;
+  // u: the largest V descale over the V blocks of the key tiles visited
+  // (1 for an empty range; a zero block descale gives rho = 0, p = 0 there)
+  // (one vector load per 64 blocks, then a max across the wave)
+  float u = 0.f;
+  if (kt0 < kt1) {
+    const int blo = kt0 * S::BN / 128, bhi = (kt1 * S::BN - 1) / 128;
+    for (int b0 = blo; b0 <= bhi; b0 += 64)
+      if (b0 + st.lane <= bhi) u = fmaxf(u, st.dv[b0 + st.lane]);
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) u = fmaxf(u, __shfl_xor(u, x));
+  }
+  const float uu = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(u)));
+  const float u_eff = uu > 0.f ? uu : 1.f;
+  st.inv_u = 1.f / u_eff;
 
   if (kt0 < kt1) {
     st.template issue_k<0>(kt0);
@@ -386,7 +453,6 @@ void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ K
     st.template run<false>(a, b);
     st.template run<true>(b, kt1);
     st.sync_tiles();
-    st.rescale();
     if ((kt1 - 1 - kt0) & 1) {
       st.template read_v<1>();
       st.template pv<1>();
@@ -396,9 +462,9 @@ void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ K
     }
   }
 
-  // ---- epilogue: O = O_acc * dv_last / (2^8 l), LSE = ln 2 * (m + log2 l)
-  const float lt = halves_sum(st.l);
-  const float inv = lt > 0.f ? st.v_unit * fast_exp2(-kPScaleLog2) / lt : 0.f;
+  // ---- epilogue: O = O_acc * u / l and LSE = ln 2 * (m_ref + log2(l) - 8)
+  const float lt = st.l;
+  const float inv = lt > 0.f ? u_eff / lt : 0.f;
   if (st.qrow < N) {
     uint16_t* orow = O + head + (size_t)st.qrow * D;
 #pragma unroll
@@ -410,10 +476,9 @@ void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ K
         for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(st.oacc[db][4 * g4 + e] * inv);
         *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * st.h) = o4;
       }
-    if (st.h == 0) {
-      const float muse = st.m == -INFINITY ? 0.f : st.m;
-      LSE[(size_t)tr.bh * N + st.qrow] = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
-    }
+    if (st.h == 0)
+      LSE[(size_t)tr.bh * N + st.qrow] =
+          lt > 0.f ? (st.m_ref + log2f(lt) - kPScaleLog2) * kLn2 : -INFINITY;
   }
 }
 
