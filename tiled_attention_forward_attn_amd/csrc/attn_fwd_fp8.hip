@@ -336,11 +336,12 @@ struct Fp8Fwd {
 };
 
 // Q and K: E4M3 codes (uint8), or bf16 (uint16) when QBF. DQ and DK are
-// unused when QBF. The bf16-score instance at d = 128 needs more than the 256
-// registers of two waves per SIMD (bf16 Q and K fragments are twice the
-// size), so it runs one workgroup per CU with the whole register file.
+// unused when QBF. Every instance runs two workgroups per CU (two waves per
+// SIMD, 256 registers each): the bf16-score instance at d = 128, whose Q and K
+// fragments are twice the size, fits since the softmax keeps no O rescale
+// state (two spilled dwords, outside the tile loops).
 template <int D, bool QBF>
-__global__ __launch_bounds__(kThreads, (QBF && D == 128) ? 1 : 2)
+__global__ __launch_bounds__(kThreads, 2)
 void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
                          const uint8_t* __restrict__ V, uint16_t* __restrict__ O,
                          float* __restrict__ LSE, const float* __restrict__ DQ,
