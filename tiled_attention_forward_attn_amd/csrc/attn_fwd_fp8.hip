@@ -10,10 +10,13 @@
 //  * a 128-row query tile is exactly one Q scaling block and a 64-key tile
 //    lies inside one K/V scaling block, so the score scale of a tile is the
 //    single number |scale| * log2(e) * dq * dk[block];
-//  * O is kept in units of u, the largest V descale of the workgroup's key
-//    range: tile t's V descale enters as rho_t = dv_t / u <= 1, folded into
-//    P, which is stored as E4M3(p * rho_t * 2^8) (2^8 and log2 rho_t are
-//    folded into the exp argument), so a new V block never rescales O;
+//  * a tile's V descale never rescales O. It is split as dv_t = f_t * 2^e_t
+//    with f_t in [1/2, 1): the mantissa enters P, stored as
+//    E4M3(p * f_t * 2^8) (2^8 and log2 f_t folded into the exp argument),
+//    and 2^e_t is the E8M0 A-operand scale of the PV MFMA (one byte, the
+//    same in every lane), so P keeps the same precision floor whatever the
+//    block descales are, and a zero descale (scale byte 0, 2^-127) still
+//    leaves P for the row sum;
 //  * the running max m of each row (log2 units) is kept as an integer, the
 //    ceiling of the exact running max, so p <= 1. Its growth is never
 //    applied to O by multiplication: O and l stay in units of a reference
@@ -30,7 +33,7 @@
 //    matrix core (one v_mfma_scale_f32_16x16x128_f8f6f4 of P^T, the PV B
 //    operand, against a constant 0/1 A operand chosen so that each lane
 //    receives the sum for the query it owns, see ones_operand), then added in
-//    fp32 with the factor 2^(m_t - m_ref) / rho_t.
+//    fp32 with the factor 2^(m_t - m_ref) / f_t.
 // A second instance (QBF) keeps Q and K in bf16 and computes S = Q K^T on the
 // bf16 matrix cores, with only V and P in E4M3: the score error that E4M3 Q
 // and K carry on data with large, aligned outlier channels (it grows with
@@ -48,7 +51,7 @@ namespace mi355attn {
 namespace {
 
 constexpr int kBN8 = 64;               // keys per tile (divides the 128-row scaling block)
-constexpr float kPScaleLog2 = 8.f;     // P is stored as E4M3(p * rho * 2^8)
+constexpr float kPScaleLog2 = 8.f;     // P is stored as E4M3(p * f * 2^8)
 constexpr float kMaxShift = 64.f;      // largest m - m_ref applied through the MFMA scale
 constexpr int kE8M0One = 127;          // E8M0 scale byte of 1.0
 
@@ -134,9 +137,9 @@ struct Fp8Fwd {
   i32x8 vf[DBLK];
   float m;           // running max (log2 units), an integer or -inf
   float m_ref;       // units of O and l (log2), -inf until m is finite
-  float inv_u;       // 1 / u, u the largest V descale of the key range
+  int sa[2];         // E8M0 byte of 2^e_t (V descale exponent) for P set 0 / 1
   int sb[2];         // E8M0 byte of 2^(m_t - m_ref) for P set 0 / 1
-  float lf[2];       // 2^(m_t - m_ref) / rho_t for P set 0 / 1
+  float lf[2];       // 2^(m_t - m_ref) / f_t for P set 0 / 1
 
   template <int ST>
   __device__ __forceinline__ void issue_k(int kt) {
@@ -236,19 +239,25 @@ struct Fp8Fwd {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
       oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db], pbuf[PB], oacc[db], 0, 0, 0,
-                                                                 kE8M0One, 0, sb[PB]);
+                                                                 sa[PB], 0, sb[PB]);
     const f32x4 rs =
         __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pbuf[PB], f32x4{}, 0, 0, 0, 0, 0, 0);
     l = fmaf(rs[0], lf[PB], l);
   }
 
-  // Online softmax of S(kt) into P set PB (E4M3 of p * rho * 2^8; byte j of
+  // Online softmax of S(kt) into P set PB (E4M3 of p * f * 2^8; byte j of
   // the operand is the key of sacc[j / 16][j % 16]).
   template <bool EDGE, int PB>
   __device__ __forceinline__ void softmax(int kt) {
     const int k0 = kt * BN;
     const float c = QBF ? cq : cq * dk[k0 / 128];   // bf16 scores carry no descale
-    const float rho = dv[k0 / 128] * inv_u;          // <= 1
+    // V descale of the tile = f * 2^(e): f in [1/2, 1) into P, 2^e into the
+    // PV A scale (E8M0 bytes 1 .. 254 cover every normal descale; zero and
+    // subnormal descales get byte 0, 2^-127, and f = 1/2)
+    const float dvt = dv[k0 / 128];
+    const int dexp = __builtin_amdgcn_frexp_expf(dvt);
+    const bool dnorm = dvt >= 1.17549435e-38f;
+    const float f = dnorm ? __builtin_amdgcn_frexp_mantf(dvt) : 0.5f;
     if constexpr (EDGE) {
       // sacc[kb][i] is key k0 + 4 h + 32 kb + 8 (i / 4) + i % 4. The allowed
       // keys of a query (key_allowed) are one range [lo, hi], computed once
@@ -289,10 +298,11 @@ struct Fp8Fwd {
       m_ref = shift > kMaxShift ? mnew : m_ref;
       shift = shift > kMaxShift ? 0.f : shift;
     }
+    sa[PB] = dnorm ? min(kE8M0One + dexp, 254) : 0;   // 255 is E8M0 NaN
     sb[PB] = kE8M0One + (int)shift;
-    lf[PB] = __builtin_ldexpf(__builtin_amdgcn_rcpf(rho), (int)shift);
-    // stored value p * rho * 2^8 = 2^(c s - (muse - 8 - log2 rho))
-    const float bias = muse - kPScaleLog2 - __builtin_amdgcn_logf(rho);
+    lf[PB] = __builtin_ldexpf(__builtin_amdgcn_rcpf(f), (int)shift);
+    // stored value p * f * 2^8 = 2^(c s - (muse - 8 - log2 f))
+    const float bias = muse - kPScaleLog2 - __builtin_amdgcn_logf(f);
     float ps[16 * NKB];
 #pragma unroll
     for (int e = 0; e < 16 * NKB; ++e) {
@@ -425,24 +435,11 @@ void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ K
   st.ones = ones_operand(st.lane);
   st.m = -INFINITY;
   st.m_ref = -INFINITY;
+  st.sa[0] = st.sa[1] = kE8M0One;
   st.sb[0] = st.sb[1] = kE8M0One;
   st.lf[0] = st.lf[1] = 0.f;
 
   const int kt0 = tr.kt0, kt1 = tr.kt1;
-  // u: the largest V descale over the V blocks of the key tiles visited
-  // (1 for an empty range; a zero block descale gives rho = 0, p = 0 there)
-  // (one vector load per 64 blocks, then a max across the wave)
-  float u = 0.f;
-  if (kt0 < kt1) {
-    const int blo = kt0 * S::BN / 128, bhi = (kt1 * S::BN - 1) / 128;
-    for (int b0 = blo; b0 <= bhi; b0 += 64)
-      if (b0 + st.lane <= bhi) u = fmaxf(u, st.dv[b0 + st.lane]);
-#pragma unroll
-    for (int x = 1; x < 64; x <<= 1) u = fmaxf(u, __shfl_xor(u, x));
-  }
-  const float uu = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(u)));
-  const float u_eff = uu > 0.f ? uu : 1.f;
-  st.inv_u = 1.f / u_eff;
 
   if (kt0 < kt1) {
     st.template issue_k<0>(kt0);
@@ -463,9 +460,9 @@ void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ K
     }
   }
 
-  // ---- epilogue: O = O_acc * u / l and LSE = ln 2 * (m_ref + log2(l) - 8)
+  // ---- epilogue: O = O_acc / l and LSE = ln 2 * (m_ref + log2(l) - 8)
   const float lt = st.l;
-  const float inv = lt > 0.f ? u_eff / lt : 0.f;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (st.qrow < N) {
     uint16_t* orow = O + head + (size_t)st.qrow * D;
 #pragma unroll
