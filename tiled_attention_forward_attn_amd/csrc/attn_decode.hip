@@ -14,9 +14,11 @@
 // S partials of every row.
 //
 // The work is a stream of K and V through HBM: every wave copies its own
-// tiles HBM -> LDS with buffer_load_dwordx4 ... lds into a private double
-// buffer (tile t+1 in flight while tile t is multiplied), so waves never
-// wait for each other and the kernel has no barrier. One wave per workgroup
+// tiles HBM -> LDS (global_load_lds_dwordx4 ... nt for tiles wholly inside
+// the sequence, buffer_load_dwordx4 ... lds with its range check for the
+// others) into a private double buffer (tile t+1 in flight while tile t is
+// multiplied), so waves never wait for each other and the kernel has no
+// barrier. One wave per workgroup
 // lets up to five waves with their copies in flight share a CU.
 //
 // Paged cache (the PagedAttention cache management that [WGC] lists among its
@@ -58,6 +60,8 @@ struct DecodeWave {
   // read one tile ahead
   const uint16_t* kpool;
   const uint16_t* vpool;
+  const uint16_t* kg;   // contiguous cache: this head's K and V
+  const uint16_t* vg;
   const __attribute__((address_space(4))) int* table;
   int head, H, page_shift, num_pages, page_next;
 
@@ -71,12 +75,44 @@ struct DecodeWave {
   bf16x8 pbuf[PST];
   float m, l;
 
+  // Tile t's copies. A tile whose BN rows all lie below k_hi (and, paged, on
+  // a page inside the pool) is read with nontemporal flat loads: its rows are
+  // inside the allocation by construction. Every other tile (the chunk's
+  // ragged end, the unused tile past it, pages outside the pool) goes through
+  // buffer descriptors, whose range check reads zeros.
   template <int ST>
   __device__ __forceinline__ void issue(int t) {
+    const int p0 = t * BN;
+    if constexpr (PAGED) {
+      const int page = page_next;
+      if (p0 + BN <= k_hi && (unsigned)page < (unsigned)num_pages) {
+        page_next = load_page(t + 1);
+        const size_t row = ((size_t)page * H + head) * ((size_t)1 << page_shift) +
+                           (p0 & ((1 << page_shift) - 1));
+        const char* kb = (const char*)(kpool + row * D);
+        const char* vb = (const char*)(vpool + row * D);
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+          copy_to_lds16_nt(kb + koff[u], kl[ST] + u * 1024);
+          copy_to_lds16_nt(vb + voff[u], vl[ST] + u * 1024);
+        }
+        return;
+      }
+    } else {
+      if (p0 + BN <= k_hi) {
+        const char* kb = (const char*)kg + (size_t)t * TILE;
+        const char* vb = (const char*)vg + (size_t)t * TILE;
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+          copy_to_lds16_nt(kb + koff[u], kl[ST] + u * 1024);
+          copy_to_lds16_nt(vb + voff[u], vl[ST] + u * 1024);
+        }
+        return;
+      }
+    }
     int soff = (int)((uint32_t)t * TILE);
     if constexpr (PAGED) {
       // descriptors over tile t's rows of its page; zero rows past k_hi
-      const int p0 = t * BN;
       uint32_t bytes = 0;
       const uint16_t* kb = kpool;
       const uint16_t* vb = vpool;
@@ -254,6 +290,8 @@ void attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     if constexpr (!PAGED) {
       st.kres = make_rsrc(K + khead, (uint32_t)Nk * D * 2);
       st.vres = make_rsrc(V + khead, (uint32_t)Nk * D * 2);
+      st.kg = K + khead;
+      st.vg = V + khead;
     }
 #pragma unroll
     for (int u = 0; u < W::LOADS; ++u) {

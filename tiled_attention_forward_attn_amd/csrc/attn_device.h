@@ -57,6 +57,16 @@ __device__ __forceinline__ void copy_to_lds16(i32x4 rsrc, const lds_char* lds_ba
                : "s"((uint32_t)(uintptr_t)lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
                : "memory", "m0");
 }
+// The same 16-byte HBM -> LDS copy from a flat global address, marked
+// nontemporal (streamed data: gfx950 accepts the nt bit on this form, not on
+// the buffer form). There is no range check: callers use it only for rows
+// they have shown to lie inside their allocation.
+__device__ __forceinline__ void copy_to_lds16_nt(const void* gaddr, const lds_char* lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :
+               : "s"((uint32_t)(uintptr_t)lds_base), "v"(gaddr)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N of this wave's vector-memory loads are outstanding.
 template <int N>
