@@ -106,7 +106,12 @@ enum {
  *             block of the corresponding E4M3 tensor, as written by
  *             attn_fp8_quantize ([WGC] section 3, per-block scaling). dtype 1
  *             needs all three; dtype 2 needs descale_v only; the others are
- *             ignored and may be NULL.
+ *             ignored and may be NULL. attn_fp8_quantize writes positive,
+ *             finite values (amax / 448, or 1 for an all-zero block). Q and K
+ *             descales enter the score scale as given. A V descale that is
+ *             zero, subnormal, negative or not finite is applied as 2^-127:
+ *             that block's keys still count in the softmax denominator, but
+ *             their values add nothing to O.
  *   stream    hipStream_t or NULL.
  *
  * dtype 2 keeps the score contraction in bf16 and only P and V in E4M3 (the

@@ -368,6 +368,27 @@ def test_fp8_running_max_grows_past_rebase(lib, causal):
     check_fp8_vs_dequantised(o, lse, codes, scale, causal, -1, f"rising causal={causal}", False)
 
 
+def test_fp8_v_descale_special_values(lib):
+    """Caller-supplied V descales of 0, +inf, NaN and -1 (attn_fp8_quantize
+    never writes them) are applied as 2^-127: those blocks' keys still count
+    in the softmax, their values add nothing. Reference: the dequantised oracle
+    with those blocks' V rows zero."""
+    N, d = 640, 128
+    q, k, v = make_qkv(1, 1, N, d, seed=77)
+    (q8, dq), (k8, dk), (v8, dv) = [lib.quantize(t.cuda()) for t in (q, k, v)]
+    bad = dv.clone()
+    bad[0, 0, 1], bad[0, 0, 2], bad[0, 0, 3], bad[0, 0, 4] = 0.0, math.inf, math.nan, -1.0
+    scale = 1 / math.sqrt(d)
+    for causal in (False, True):
+        o, lse = lib.fwd(q8, k8, v8, descales=(dq, dk, bad), causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        dv_ref = dv.cpu().numpy().copy()
+        dv_ref[0, 0, 1:5] = 0.0
+        codes = [t.cpu().numpy() for t in (q8, dq, k8, dk, v8)] + [dv_ref]
+        check_fp8_vs_dequantised(o.cpu(), lse.cpu(), codes, scale, causal, -1,
+                                 f"special V descales causal={causal}", False)
+
+
 @pytest.mark.parametrize("zero_block", [False, True])
 def test_fp8_v_blocks_far_apart(lib, zero_block):
     """V blocks whose descales span six orders of magnitude (and one all-zero

@@ -256,7 +256,7 @@ struct Fp8Fwd {
     // subnormal descales get byte 0, 2^-127, and f = 1/2)
     const float dvt = dv[k0 / 128];
     const int dexp = __builtin_amdgcn_frexp_expf(dvt);
-    const bool dnorm = dvt >= 1.17549435e-38f;
+    const bool dnorm = dvt >= 1.17549435e-38f && dvt <= 3.40282347e+38f;   // positive, normal, finite
     const float f = dnorm ? __builtin_amdgcn_frexp_mantf(dvt) : 0.5f;
     if constexpr (EDGE) {
       // sacc[kb][i] is key k0 + 4 h + 32 kb + 8 (i / 4) + i % 4. The allowed
