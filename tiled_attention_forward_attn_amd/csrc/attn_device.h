@@ -269,22 +269,9 @@ __device__ __forceinline__ InteriorSpan interior_span(const TileRange& t, int N,
   return s;
 }
 
-// True if some (query, key) pair of the key tile starting at k0 is disallowed
-// for some query of the tile (or lies beyond N): only such tiles evaluate the
-// element mask.
-__device__ __forceinline__ bool tile_is_edge(const TileRange& t, int k0, int N, int causal,
-                                             int window) {
-  return (k0 + kBN > N) || (causal && k0 + kBN - 1 > t.q0) ||
-         (window >= 0 && (k0 < t.q_last - window || (!causal && k0 + kBN - 1 > t.q0 + window)));
-}
-
-// The band of the sliding-window page: keys i - w .. i + w, cut at j <= i when
-// causal; window < 0 disables the band.
-__device__ __forceinline__ bool key_allowed(int key, int qrow, int N, int causal, int window) {
-  bool ok = key < N;
-  if (causal) ok = ok && key <= qrow;
-  if (window >= 0) ok = ok && key >= qrow - window && (causal || key <= qrow + window);
-  return ok;
-}
+// The allowed keys of query i (the band of the sliding-window page, both ends
+// inclusive): j < N; j <= i when causal; with a window w >= 0 also
+// j >= i - w and, when not causal, j <= i + w. For every query this is one
+// range [lo, hi], which the kernels' edge-tile masks compute once per lane.
 
 }  // namespace mi355attn

@@ -168,8 +168,8 @@ struct Bf16Fwd {
 
   // Disallowed keys of an edge tile get score -inf. sacc[b][kb][i] is the
   // score of key base + 32 kb + 8 (i/4) + i%4 (base = k0 + 4 h) against query
-  // qrow[b]. The allowed keys of a query form one range [lo, hi] (key_allowed:
-  // below N, causal or band upper edge, band lower edge), so each lane
+  // qrow[b]. The allowed keys of a query form one range [lo, hi] (below N;
+  // the causal or band upper edge; the band lower edge), so each lane
   // computes that range once per tile and each element needs two compares
   // against a constant offset.
   __device__ __forceinline__ void mask(int kt) {

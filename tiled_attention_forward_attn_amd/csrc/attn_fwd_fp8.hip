@@ -260,8 +260,9 @@ struct Fp8Fwd {
     const float f = dnorm ? __builtin_amdgcn_frexp_mantf(dvt) : 0.5f;
     if constexpr (EDGE) {
       // sacc[kb][i] is key k0 + 4 h + 32 kb + 8 (i / 4) + i % 4. The allowed
-      // keys of a query (key_allowed) are one range [lo, hi], computed once
-      // per lane; each element then needs two compares against a constant.
+      // keys of a query are one range [lo, hi] (below N; the causal or band
+      // upper edge; the band lower edge), computed once per lane; each
+      // element then needs two compares against a constant.
       const int base = k0 + 4 * h;
       const int w = min(window, N);   // a band wider than N cuts nothing
       int hi = N - 1;
