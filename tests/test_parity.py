@@ -368,6 +368,60 @@ def test_fp8_running_max_grows_past_rebase(lib, causal):
     check_fp8_vs_dequantised(o, lse, codes, scale, causal, -1, f"rising causal={causal}", False)
 
 
+MAX_N_ROWS = lambda N: [0, 1, 1023, 1024, 4097, N // 2, N // 2 + 777, N - 1025, N - 2, N - 1]
+
+
+@pytest.mark.parametrize("d,N", [(64, 1 << 23), (128, 1 << 23), (256, 1 << 22)])
+def test_bf16_max_n_window(lib, d, N):
+    """The largest N the C ABI accepts at each head dimension (ATTN_MAX_N,
+    ATTN_MAX_N_D256), causal with a 1024-key window so the work stays small:
+    tile offsets and buffer ranges at their 32-bit limits. Inputs from torch's
+    seeded CUDA generator (3 N d values); sampled rows against the oracle on
+    each row's key band, which is exactly its allowed set."""
+    g = torch.Generator(device="cuda").manual_seed(90 + d)
+    q, k, v = [torch.randn((1, 1, N, d), generator=g, device="cuda").to(torch.bfloat16)
+               for _ in range(3)]
+    w, scale = 1024, 1 / math.sqrt(d)
+    o, lse = lib.fwd(q, k, v, causal=True, window=w, scale=scale)
+    torch.cuda.synchronize()
+    for i in MAX_N_ROWS(N):
+        lo = max(0, i - w)
+        sl = lambda t, a, b_: t[:, :, a:b_].cpu()
+        ref_o, ref_lse = attention_two_pass(sl(q, i, i + 1), sl(k, lo, i + 1), sl(v, lo, i + 1), scale)
+        check_bf16(o[:, :, i:i + 1].cpu(), lse[:, :, i:i + 1].cpu(), ref_o, ref_lse, f"N={N} d={d} row {i}")
+    del q, k, v, o, lse
+
+
+def test_fp8_max_n_window(lib):
+    """All-E4M3 attention at N = ATTN_MAX_N, d = 128, causal window 1024:
+    the quantiser and the fp8 kernel at their largest offsets. Sampled rows
+    inside the P-rounding bound of the oracle on the dequantised band."""
+    N, d, w = 1 << 23, 128, 1024
+    g = torch.Generator(device="cuda").manual_seed(95)
+    x = [torch.randn((1, 1, N, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3)]
+    (q8, dq), (k8, dk), (v8, dv) = [lib.quantize(t) for t in x]
+    del x
+    scale = 1 / math.sqrt(d)
+    o, lse = lib.fwd(q8, k8, v8, descales=(dq, dk, dv), causal=True, window=w, scale=scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+
+    def deq(codes, desc, a, b_):   # rows a .. b_ - 1, from a 128-row block boundary
+        a0 = a // 128 * 128
+        c = codes[:, :, a0:b_].cpu().view(torch.uint8).numpy()
+        s_ = desc[:, :, a0 // 128:(b_ - 1) // 128 + 1].cpu().numpy()
+        return torch.from_numpy(dequantize(c, s_))[0, 0, a - a0:]
+
+    for i in MAX_N_ROWS(N):
+        lo = max(0, i - w)
+        qd, kd, vd = deq(q8, dq, i, i + 1), deq(k8, dk, lo, i + 1), deq(v8, dv, lo, i + 1)
+        ref_o, _ = attention_two_pass(qd[None, None], kd[None, None], vd[None, None], scale)
+        bound, _ = fp8_output_bound(qd, kd, vd, ref_o[0, 0], scale, False, -1, rows=[0])
+        err = (o[0, 0, i:i + 1].cpu().double() - ref_o[0, 0]).abs()
+        assert float((err - bound).max()) <= 0, f"row {i}: excess {float((err - bound).max()):.3e}"
+    del q8, k8, v8, o, lse
+
+
 def test_fp8_v_descale_special_values(lib):
     """Caller-supplied V descales of 0, +inf, NaN and -1 (attn_fp8_quantize
     never writes them) are applied as 2^-127: those blocks' keys still count
