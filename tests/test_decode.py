@@ -45,6 +45,23 @@ def test_decode_vs_oracle(lib, B, H, Nq, Nk, d, causal, splits):
     check(o, lse, ref_o, ref_lse, f"{(B, H, Nq, Nk, d, causal, splits)}")
 
 
+def test_decode_max_nk(lib):
+    """Nk = 2^23 (ATTN_MAX_N), the longest cache the C ABI accepts: the copies'
+    offsets and buffer ranges at their limits, and the nontemporal flat copies
+    of interior tiles at their largest addresses. Two queries, d = 64, causal,
+    the default split count. Inputs from torch's seeded CUDA generator
+    (2 Nk d values); oracle in fp64 on the host."""
+    Nk, Nq, d = 1 << 23, 2, 64
+    g = torch.Generator(device="cuda").manual_seed(97)
+    q, k, v = [torch.randn((1, 1, n, d), generator=g, device="cuda").to(torch.bfloat16)
+               for n in (Nq, Nk, Nk)]
+    o, lse = lib.decode(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = attention_decode(q.cpu(), k.cpu(), v.cpu(), 1 / math.sqrt(d), causal=True)
+    check(o, lse, ref_o, ref_lse, "Nk = 2^23")
+    del q, k, v, o, lse
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.4, 1.1])
 def test_decode_scales(lib, scale):
     q, k, v = decode_inputs(1, 2, 4, 700, 128, seed=5)
