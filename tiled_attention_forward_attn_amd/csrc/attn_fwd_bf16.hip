@@ -322,8 +322,19 @@ struct Bf16Fwd {
 
 // PAIRED: each workgroup runs a causal tile pair (see TilePair); otherwise
 // one query tile per workgroup (order: see tile_range).
+// Workgroups per CU: two waves per SIMD (8 / NW workgroups), except the d = 64
+// single-tile instance, which fits 168 registers with its tile loops free of
+// spills and runs three 4-wave workgroups per CU: at d = 64 a workgroup has
+// half the MFMA work per key tile, so its fixed entry and drain costs weigh
+// more, and a third resident workgroup covers them (banded masks most).
 template <int D, int BN, int QB, int NW, bool PAIRED>
-__global__ __launch_bounds__(64 * NW, (QB == 1 && D <= 128) ? 8 / NW : 1)
+constexpr int bf16_wg_per_cu() {
+  if (QB != 1 || D > 128) return 1;
+  return (D == 64 && NW == 4 && !PAIRED) ? 3 : 8 / NW;
+}
+
+template <int D, int BN, int QB, int NW, bool PAIRED>
+__global__ __launch_bounds__(64 * NW, (bf16_wg_per_cu<D, BN, QB, NW, PAIRED>()))
 void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                           float* __restrict__ LSE, int N, int nqt, float c, int causal,
