@@ -7,9 +7,9 @@
 // scaling, FP32 accumulation, BF16 output).
 //
 // Dequantisation is folded into scalars, never applied per element:
-//  * a 128-row query tile is exactly one Q scaling block and a 64-key tile
-//    lies inside one K/V scaling block, so the score scale of a tile is the
-//    single number |scale| * log2(e) * dq * dk[block];
+//  * a 128-row query tile is exactly one Q scaling block and a 64- or
+//    128-key tile lies inside one K/V scaling block, so the score scale of a
+//    tile is the single number |scale| * log2(e) * dq * dk[block];
 //  * a tile's V descale never rescales O. It is split as dv_t = f_t * 2^e_t
 //    with f_t in [1/2, 1): the mantissa enters P, stored as
 //    E4M3(p * f_t * 2^8) (2^8 and log2 f_t folded into the exp argument),
@@ -50,7 +50,11 @@
 namespace mi355attn {
 namespace {
 
-constexpr int kBN8 = 64;               // keys per tile (divides the 128-row scaling block)
+// Keys per tile; each size divides the 128-row scaling block. E4M3 at
+// d = 128 takes 128-key tiles (half the per-tile softmax and barrier work
+// per key); the others keep 64, where 128 would not fit the registers.
+template <int D, bool QBF>
+constexpr int fp8_bn() { return (D == 128 && !QBF) ? 128 : 64; }
 constexpr float kPScaleLog2 = 8.f;     // P is stored as E4M3(p * f * 2^8)
 constexpr float kMaxShift = 64.f;      // largest m - m_ref applied through the MFMA scale
 constexpr int kE8M0One = 127;          // E8M0 scale byte of 1.0
@@ -99,7 +103,8 @@ __device__ __forceinline__ int cvt4(float a, float b, float c, float d) {
 template <int D, bool QBF>
 struct Fp8Fwd {
   using QKFrag = std::conditional_t<QBF, bf16x8, i32x8>;
-  static constexpr int BN = kBN8;
+  static constexpr int BN = fp8_bn<D, QBF>();
+  static constexpr int NH = BN / 64;                         // 64-key halves (one PV MFMA k-step)
   static constexpr int KSTEPS = QBF ? D / 16 : D / 64;      // MFMA k-steps of QK^T
   static constexpr int DBLK = D / 32;                       // 32-wide d blocks of O^T
   static constexpr int NKB = BN / 32;                       // 32-key blocks of S^T
@@ -132,7 +137,7 @@ struct Fp8Fwd {
   float l;            // row sum, units of 2^(m_ref - 8) (both key halves)
   i32x8 ones;
   f32x16 sacc[NKB];
-  i32x8 pbuf[2];
+  i32x8 pbuf[2][NH];
   QKFrag kf[NKB][KSTEPS];
   i32x8 vf[DBLK];
   float m;           // running max (log2 units), an integer or -inf
@@ -174,10 +179,11 @@ struct Fp8Fwd {
       }
     }
   }
-  // A operand of O^T += V^T P^T: lane (d, h) reads LDS rows 16t + 8h .. +7 of
-  // column d for t = 0..3 (the swapped key order makes these its P's keys).
+  // A operand of O^T += V^T P^T for the 64-key half hh: lane (d, h) reads LDS
+  // rows 64 hh + 16t + 8h .. +7 of column d for t = 0..3 (the swapped key
+  // order makes these its P's keys).
   template <int ST>
-  __device__ __forceinline__ void read_v() {
+  __device__ __forceinline__ void read_v(int hh) {
     const lds_char* Vs = vl[ST];
     const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
@@ -185,7 +191,7 @@ struct Fp8Fwd {
       const int col = db * 32 + 16 * (g & 1) + 8 * (sl & 1);  // this source lane's 8 bytes
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int r = 16 * t + 8 * (g >> 1) + (sl >> 1);
+        const int r = 64 * hh + 16 * t + 8 * (g >> 1) + (sl >> 1);
         const int a = r * D + (((col >> 4) ^ swz_v8<D>(r)) << 4) + (col & 15);
         const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(Vs + a));
         vf[db][2 * t] = x[0];
@@ -235,18 +241,29 @@ struct Fp8Fwd {
   }
 
   template <int PB>
-  __device__ __forceinline__ void pv() {
+  __device__ __forceinline__ void pv(int hh) {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db], pbuf[PB], oacc[db], 0, 0, 0,
-                                                                 sa[PB], 0, sb[PB]);
-    const f32x4 rs =
-        __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pbuf[PB], f32x4{}, 0, 0, 0, 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[db], pbuf[PB][hh], oacc[db], 0, 0,
+                                                                 0, sa[PB], 0, sb[PB]);
+    const f32x4 rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pbuf[PB][hh], f32x4{}, 0,
+                                                                      0, 0, 0, 0, 0);
     l = fmaf(rs[0], lf[PB], l);
+  }
+  // PV of P set PB, V stage PB: halves after the first read their V
+  // fragments here (the first half's are read ahead by the caller)
+  template <int PB>
+  __device__ __forceinline__ void pv_rest() {
+    pv<PB>(0);
+#pragma unroll
+    for (int hh = 1; hh < NH; ++hh) {
+      read_v<PB>(hh);
+      pv<PB>(hh);
+    }
   }
 
   // Online softmax of S(kt) into P set PB (E4M3 of p * f * 2^8; byte j of
-  // the operand is the key of sacc[j / 16][j % 16]).
+  // half hh's operand is the key of sacc[2 hh + j / 16][j % 16]).
   template <bool EDGE, int PB>
   __device__ __forceinline__ void softmax(int kt) {
     const int k0 = kt * BN;
@@ -311,8 +328,8 @@ struct Fp8Fwd {
       if constexpr (EDGE) ps[e] = sv[e] == -INFINITY ? 0.f : ps[e];
     }
 #pragma unroll
-    for (int w = 0; w < 8; ++w)
-      pbuf[PB][w] = cvt4(ps[4 * w], ps[4 * w + 1], ps[4 * w + 2], ps[4 * w + 3]);
+    for (int w = 0; w < 8 * NH; ++w)
+      pbuf[PB][w / 8][w % 8] = cvt4(ps[4 * w], ps[4 * w + 1], ps[4 * w + 2], ps[4 * w + 3]);
     m = mnew;
   }
 
@@ -327,9 +344,9 @@ struct Fp8Fwd {
     sync_tiles();                           // K_j, V_{j-1} landed; iteration j-1 done
     issue_k<PB ^ 1>(j + 1);                 // unconditional: see the bf16 kernel
     issue_v<PB>(j);
-    if constexpr (!FIRST) read_v<PB ^ 1>();
+    if constexpr (!FIRST) read_v<PB ^ 1>(0);
     read_k_qk<PB>();
-    if constexpr (!FIRST) pv<PB ^ 1>();
+    if constexpr (!FIRST) pv_rest<PB ^ 1>();
     softmax<EDGE, PB>(j);
     __builtin_amdgcn_iglp_opt(0);
   }
@@ -453,11 +470,11 @@ void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ K
     st.template run<true>(b, kt1);
     st.sync_tiles();
     if ((kt1 - 1 - kt0) & 1) {
-      st.template read_v<1>();
-      st.template pv<1>();
+      st.template read_v<1>(0);
+      st.template pv_rest<1>();
     } else {
-      st.template read_v<0>();
-      st.template pv<0>();
+      st.template read_v<0>(0);
+      st.template pv_rest<0>();
     }
   }
 
