@@ -50,11 +50,11 @@
 namespace mi355attn {
 namespace {
 
-// Keys per tile; each size divides the 128-row scaling block. E4M3 at
-// d = 128 takes 128-key tiles (half the per-tile softmax and barrier work
-// per key); the others keep 64, where 128 would not fit the registers.
+// Keys per tile; each size divides the 128-row scaling block. E4M3 takes
+// 128-key tiles (half the per-tile softmax and barrier work per key); the
+// bf16-score instance keeps 64, where 128 would not fit the registers.
 template <int D, bool QBF>
-constexpr int fp8_bn() { return (D == 128 && !QBF) ? 128 : 64; }
+constexpr int fp8_bn() { return !QBF ? 128 : 64; }
 constexpr float kPScaleLog2 = 8.f;     // P is stored as E4M3(p * f * 2^8)
 constexpr float kMaxShift = 64.f;      // largest m - m_ref applied through the MFMA scale
 constexpr int kE8M0One = 127;          // E8M0 scale byte of 1.0
