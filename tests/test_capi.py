@@ -163,6 +163,20 @@ def test_binding_checks_before_calling(lib):
         tafa.quantize(q)
 
 
+def test_binding_buffer_check_refuses_host_memory():
+    # the check every caller-supplied output, descale and workspace goes
+    # through: a host tensor for a device pointer is refused (the shape and
+    # dtype refusals are exercised on the GPU, where device tensors exist)
+    import torch
+    t = torch.zeros(2, 3, dtype=torch.float32)
+    with pytest.raises(ValueError, match="must be on"):
+        tafa._check_buf("out", t, (2, 3), (torch.float32,), torch.device("cuda:0"))
+    with pytest.raises(ValueError, match="must be a torch.Tensor"):
+        tafa._check_buf("lse", [0.0], (1,), (torch.float32,), torch.device("cuda:0"))
+    with pytest.raises(ValueError, match="workspace"):
+        tafa._workspace(torch.zeros(16, dtype=torch.uint8), 16, torch.device("cuda:0"))
+
+
 def call_merge(lib, op=A, lp=A + GAP, o=A + 2 * GAP, lse=A + 3 * GAP, R=3, B=2, H=3, N=300, d=128):
     return lib.attn_lse_merge(op, lp, o, lse, R, B, H, N, d, None)
 

@@ -92,6 +92,23 @@ def _check_4d(name: str, t: torch.Tensor):
         raise ValueError(f"{name} must be a contiguous 4-D [B, H, N, d] CUDA tensor")
 
 
+def _check_buf(name: str, t: torch.Tensor, shape, dtypes, device: torch.device):
+    """A caller-supplied output or auxiliary tensor must be exactly what the
+    kernels read or write through its pointer: on the inputs' device,
+    contiguous, of this shape and dtype. Raises ValueError otherwise (before
+    any launch)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(map(str, dtypes))}, got {t.dtype}")
+
+
 def _is_fp8(t: torch.Tensor) -> bool:
     return t.dtype in (torch.uint8, torch.float8_e4m3fn)
 
@@ -110,6 +127,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         _check_4d(name, t)
     if not (q.shape == k.shape == v.shape):
         raise ValueError("q, k and v must have the same shape")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
     B, H, N, d = q.shape
     q8, k8, v8 = _is_fp8(q), _is_fp8(k), _is_fp8(v)
     bf = [t.dtype == torch.bfloat16 for t in (q, k, v)]
@@ -128,13 +147,21 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
             raise ValueError("all-E4M3 inputs need dq and dk")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     dq, dk, dv = descales if dtype != DTYPE_BF16 else (None, None, None)
     if dtype == DTYPE_FP8_PV:
         dq = dk = None
+    nsb = -(-N // BLOCK_ROWS)
+    for name, t in (("descale_q", dq), ("descale_k", dk), ("descale_v", dv)):
+        if t is not None:
+            _check_buf(name, t, (B, H, nsb), (torch.float32,), q.device)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    else:
+        _check_buf("out", out, (B, H, N, d), (torch.bfloat16,), q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_buf("lse", lse, (B, H, N), (torch.float32,), q.device)
     rc = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                          int(causal), int(window), float(scale), dtype,
                          _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream))
@@ -152,8 +179,12 @@ def quantize(x: torch.Tensor, per_tensor: bool = False, out: torch.Tensor | None
     B, H, N, d = x.shape
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    else:
+        _check_buf("out", out, (B, H, N, d), (torch.uint8, torch.float8_e4m3fn), x.device)
     if descale is None:
         descale = torch.empty((B, H, -(-N // BLOCK_ROWS)), dtype=torch.float32, device=x.device)
+    else:
+        _check_buf("descale", descale, (B, H, -(-N // BLOCK_ROWS)), (torch.float32,), x.device)
     rc = load().attn_fp8_quantize(_ptr(x), _ptr(out), _ptr(descale), B, H, N, d,
                                   int(per_tensor), _stream(stream))
     if rc != 0:
@@ -174,11 +205,17 @@ def merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: torch.Tensor | No
     for name, t in (("o_parts", o_parts), ("lse_parts", lse_parts)):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
+    if lse_parts.device != o_parts.device:
+        raise ValueError("o_parts and lse_parts must be on the same device")
     R, B, H, N, d = o_parts.shape
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=o_parts.device)
+    else:
+        _check_buf("out", out, (B, H, N, d), (torch.bfloat16,), o_parts.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    else:
+        _check_buf("lse", lse, (B, H, N), (torch.float32,), o_parts.device)
     rc = load().attn_lse_merge(_ptr(o_parts), _ptr(lse_parts), _ptr(out), _ptr(lse), R, B, H, N, d,
                                _stream(stream))
     if rc != 0:
@@ -187,6 +224,17 @@ def merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: torch.Tensor | No
 
 
 MAX_DECODE_Q = 32
+
+
+def _workspace(ws: torch.Tensor | None, need: int, device: torch.device) -> torch.Tensor:
+    """The decode workspace: allocated here when not given; a caller's must be
+    a contiguous device tensor on the inputs' device (its byte size goes to the
+    C ABI, which rejects one that is too small)."""
+    if ws is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return ws
 
 
 def default_splits(B: int, H: int, Nk: int) -> int:
@@ -211,18 +259,23 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = 
     Nk = k.shape[2]
     if k.shape != (B, H, Nk, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if splits is None:
         splits = default_splits(B, H, Nk)
     lib = load()
     need = lib.attn_decode_workspace_bytes(B, H, Nq, d, splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     if out is None:
         out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device)
+    else:
+        _check_buf("out", out, (B, H, Nq, d), (torch.bfloat16,), q.device)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        _check_buf("lse", lse, (B, H, Nq), (torch.float32,), q.device)
     rc = lib.attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d,
                          int(causal), float(scale), int(splits), _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _stream(stream))
@@ -258,6 +311,8 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
             raise ValueError(f"{name} must have shape {shape}")
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_pages]")
+    if not (q.device == k_cache.device == v_cache.device):
+        raise ValueError("q, k_cache and v_cache must be on the same device")
     max_pages = block_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -265,12 +320,15 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         splits = default_splits(B, H, max_pages * page_size)
     lib = load()
     need = lib.attn_decode_workspace_bytes(B, H, Nq, d, splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     if out is None:
         out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device)
+    else:
+        _check_buf("out", out, (B, H, Nq, d), (torch.bfloat16,), q.device)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        _check_buf("lse", lse, (B, H, Nq), (torch.float32,), q.device)
     rc = lib.attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                _ptr(seq_lens), _ptr(out), _ptr(lse), B, H, Nq, d, num_pages,
                                page_size, max_pages, int(causal), float(scale), int(splits),
