@@ -62,9 +62,9 @@ enum {
 };
 
 /* Largest supported sizes (index arithmetic is 64-bit; these bound the grid). */
-/* Longest sequence: one head's K or V plus a tile past its end must stay
- * inside the 32-bit byte range of the buffer descriptors the kernels read
- * through ((2^23 + 64) * 128 * 2 < 2^32). */
+/* Longest sequence: the byte offset of a tile past one head's K or V end
+ * must stay inside the 32-bit range of the buffer descriptors the kernels
+ * read through ((2^23 + 128) * 128 * 2 < 2^32). */
 #define ATTN_MAX_N (1 << 23)
 /* The same bound at d = 256, where a row is twice as long. */
 #define ATTN_MAX_N_D256 (1 << 22)
@@ -107,7 +107,8 @@ enum {
  *             attn_fp8_quantize ([WGC] section 3, per-block scaling). dtype 1
  *             needs all three; dtype 2 needs descale_v only; the others are
  *             ignored and may be NULL. attn_fp8_quantize writes positive,
- *             finite values (amax / 448, or 1 for an all-zero block). Q and K
+ *             normal, finite values (amax / 448, at least 2^-126; 1 for an
+ *             all-zero block). Q and K
  *             descales enter the score scale as given. A V descale that is
  *             zero, subnormal, negative or not finite is applied as 2^-127:
  *             that block's keys still count in the softmax denominator, but
@@ -257,8 +258,11 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  * For each (b, h) and each block of 128 rows (the last block may be shorter):
  *   amax = max |x| over the block (per_tensor = 1: over the whole tensor)
  *   r = fp32(448 / amax), descale = fp32(amax / 448); amax == 0 gives r = 1,
- *   descale = 1
+ *   descale = 1; 0 < amax < 448 * 2^-126 (where amax / 448 would not be a
+ *   normal fp32) gives descale = 2^-126 and r = 2^126, its exact reciprocal
  *   x8 = E4M3(fp32(x * r)), round to nearest even, saturating at +-448
+ * So every descale is a positive, normal, finite fp32 value and a zero
+ * element always encodes as 0.
  * [WGC] section 3 (dynamic per-block scaling into the range of max 448, fp32
  * accumulation downstream); the format is [JJ] section 1.5's E4M3.
  *

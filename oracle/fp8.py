@@ -21,6 +21,16 @@ rescales QK^T). For each block of 128 rows x d of one (batch, head):
     descale = fp32(amax / 448)
     code    = e4m3(fp32(x * r))          (fp32 product, then RNE to E4M3)
     amax == 0  =>  r = 1, descale = 1 (all codes 0)
+    0 < amax < 448 * 2^-126  =>  r = 2^126, descale = 2^-126
+
+The pages say nothing of blocks this small. There amax / 448 would lie below
+the smallest normal fp32 and 448 / amax would overflow (to +inf once amax <
+448 / FLT_MAX, which turns 0 * r into NaN). The reading taken: the descale
+never goes below the smallest normal fp32, 2^-126, and r is its exact
+reciprocal. Every |x * r| is then below 448, so nothing saturates, zeros
+encode as 0 and code * descale still approximates x (the tiny values keep
+fewer significant bits, as E4M3 subnormals). At amax = 448 * 2^-126 exactly
+both rules give the same r and descale.
 
 The fp32 steps are those the GPU quantiser takes: where a floating-point
 operation decides an integer code, both sides decide it in the same precision.
@@ -39,6 +49,8 @@ E4M3_EXP_BITS = 4           # [JJ] section 1.5
 E4M3_MAN_BITS = 3           # [JJ] section 1.5
 E4M3_BIAS = 7
 QUANT_BLOCK_ROWS = 128
+FP32_MIN_NORMAL = 2.0 ** -126
+AMAX_MIN_NORMAL = E4M3_MAX * FP32_MIN_NORMAL     # 7 * 2^-120, exact in fp32
 
 
 def e4m3_decode(code: int) -> float:
@@ -112,6 +124,9 @@ def quantize(x, per_tensor: bool = False, block_rows: int = QUANT_BLOCK_ROWS):
                 if amax == 0:
                     r = np.float32(1.0)
                     ds = np.float32(1.0)
+                elif amax < np.float32(AMAX_MIN_NORMAL):
+                    r = np.float32(1.0 / FP32_MIN_NORMAL)
+                    ds = np.float32(FP32_MIN_NORMAL)
                 else:
                     r = np.float32(f448 / amax)
                     ds = np.float32(amax / f448)

@@ -141,3 +141,61 @@ def test_per_tensor_descales_are_uniform():
     _, ds = quantize(x, per_tensor=True)
     assert np.all(ds == ds.flat[0])
     assert ds.flat[0] == np.float32(float(x.float().abs().max()) / 448.0)
+
+
+# ---- blocks at every magnitude, including those whose amax / 448 would not
+# be a normal fp32 (the quantiser's reading for 0 < amax < 448 * 2^-126)
+
+MAGNITUDES = [2.0 ** -133, 1e-39, 1e-37, 3e-36, 5.2e-36, 7 * 2.0 ** -120, 5.3e-36, 1e-20, 1e-3, 1.0,
+              300.0, 1e30, 3.0e38]
+
+
+def _block_of(amax, n=128, d=16, seed=0):
+    """A 128 x d block of values in [-amax, amax] (bf16), its largest magnitude
+    amax itself (when amax is a bf16 value), with a few exact zeros."""
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.rand(n, d, generator=g, dtype=torch.float64) * 2 - 1) * amax
+    x[0, 0] = amax
+    x[3, :4] = 0.0
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("amax", MAGNITUDES)
+def test_quantize_round_trip_bound_at_every_magnitude(amax):
+    """code * descale reproduces x within E4M3's rounding at any block scale:
+    |deq - x| <= (2^-4 + 2^-21) |x| + 2^-10 descale (half a mantissa step in
+    the normal range, half the subnormal step 2^-9 in code units, and the fp32
+    roundings of r, descale and x * r). Zeros stay zero, no code is NaN and
+    every descale is a positive normal fp32 number."""
+    x = _block_of(amax)[None, None]
+    codes, ds = quantize(x)
+    tab = e4m3_decode_table()
+    assert not np.isnan(tab[codes]).any()
+    d = float(ds[0, 0, 0])
+    assert 2.0 ** -126 <= d < math.inf
+    deq = dequantize(codes, ds)
+    xf = x.double().numpy()
+    assert np.all(deq[xf == 0] == 0)
+    bound = (2.0 ** -4 + 2.0 ** -21) * np.abs(xf) + 2.0 ** -10 * d
+    assert np.all(np.abs(deq - xf) <= bound)
+
+
+def test_quantize_tiny_block_rule():
+    """0 < amax < 448 * 2^-126: descale 2^-126 and r = 2^126 exactly, so the
+    codes are those of x * 2^126 (exact in fp32) and nothing saturates."""
+    for amax in (1e-37, 3e-36, 2.0 ** -130):
+        x = _block_of(amax, seed=1)[None, None]
+        codes, ds = quantize(x)
+        assert ds[0, 0, 0] == np.float32(2.0 ** -126)
+        y = (x.double() * 2.0 ** 126).float().numpy()
+        assert np.array_equal(codes, torch_codes(y))
+        assert np.abs(e4m3_decode_table()[codes]).max() < 448.0
+    # at amax = 448 * 2^-126 exactly, the ordinary rule gives the same numbers
+    x = _block_of(7 * 2.0 ** -120, seed=2)[None, None]
+    codes, ds = quantize(x)
+    assert ds[0, 0, 0] == np.float32(2.0 ** -126)
+    assert np.array_equal(codes, torch_codes((x.double() * 2.0 ** 126).float().numpy()))
+    # per tensor: a tiny global amax takes the same rule in every slot
+    x = torch.cat([_block_of(1e-37, seed=3), _block_of(2e-38, seed=4)])[None, None]
+    _, ds = quantize(x, per_tensor=True)
+    assert np.all(ds == np.float32(2.0 ** -126))

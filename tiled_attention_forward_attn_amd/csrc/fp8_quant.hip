@@ -5,7 +5,10 @@
 // (batch, head):
 //   amax = max |x|, r = fp32(448 / amax), descale = fp32(amax / 448)
 //   code = E4M3(fp32(x * r)), round to nearest even, saturating at +-448
-//   (amax == 0: r = 1, descale = 1)
+//   (amax == 0: r = 1, descale = 1; 0 < amax < 448 * 2^-126, where amax / 448
+//   would not be a normal fp32 and 448 / amax could overflow: r = 2^126,
+//   descale = 2^-126, its exact reciprocal, so every |x * r| < 448 and a
+//   zero encodes as 0)
 // The divisions are IEEE correctly rounded (the library is built without
 // fast-math), the product is one fp32 multiply, and the conversion is
 // v_cvt_pk_fp8_f32 (round to nearest even, OCP E4M3FN on gfx950) after a clamp
@@ -37,6 +40,9 @@ typedef __attribute__((ext_vector_type(2))) int i32x2;
 constexpr int kRows = 128;  // rows per scaling block
 constexpr int kThreads = 256;
 constexpr float kE4M3Max = 448.0f;
+constexpr float kAmaxMinNormal = 0x1.cp-118f;   // 448 * 2^-126 = 7 * 2^-120
+constexpr float kMinNormal = 0x1p-126f;
+constexpr float kMinNormalInv = 0x1p126f;
 
 enum Mode { kPerBlock = 0, kAmaxOnly = 1, kConvertFromSlot = 2 };
 
@@ -98,7 +104,8 @@ void fp8_quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
     }
   }
 
-  const float r = amax == 0.f ? 1.f : kE4M3Max / amax;
+  const bool tiny = amax < kAmaxMinNormal;   // includes amax == 0
+  const float r = amax == 0.f ? 1.f : (tiny ? kMinNormalInv : kE4M3Max / amax);
 #pragma unroll
   for (int u = 0; u < LOADS; ++u) {
     const int chunk = tid + u * kThreads;
@@ -112,7 +119,7 @@ void fp8_quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
       __builtin_nontemporal_store(out, (i32x2*)(X8 + head + (size_t)row * D + col * 8));
     }
   }
-  if (tid == 0) descale[blk] = amax == 0.f ? 1.f : amax / kE4M3Max;
+  if (tid == 0) descale[blk] = amax == 0.f ? 1.f : (tiny ? kMinNormal : amax / kE4M3Max);
 }
 
 // One workgroup: global max over all slots, written back into every slot.
