@@ -25,9 +25,13 @@ Sources (web pages on FlashAttention-3, cited by title and section):
   [JJ]   "大模型加速-核心网络算子-Flash Attention V3"
   [YT]   "FlashAttention V3：优化框架吞吐量的关键技术实践"
 
-Every function in this package is pinned by tests (``tests/test_oracle*.py``
-and ``tests/test_fp8_model.py``) against library routines, closed forms,
-invariants and brute force; none is "parity unpinned".
+Every function in this package is pinned by CPU tests against something
+other than itself: the attention, decode, paged and merge oracles by library
+routines, closed forms, invariants and brute force (``tests/test_oracle*.py``),
+the E4M3 model and the quantiser by torch's float8 type, the format facts the
+pages print and the quantiser's defining error bound at every block magnitude
+(``tests/test_fp8_model.py``), and the error measures by closed-form cases
+(``tests/test_oracle_metrics.py``).
 """
 from .attention import (allowed_range, attention_two_pass, attention_online,
                         probabilities, attention_rows)

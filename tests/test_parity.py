@@ -195,9 +195,11 @@ def test_workload_full_compare(lib, name):
     check_bf16(o, lse, ref_o, ref_lse, name)
 
 
+SPREAD_16 = [(i, (7 * i + 3) % 16) for i in range(16)]   # every batch once, heads spread
+
+
 @pytest.mark.parametrize("name,heads", [
-    ("noncausal_b16h16n8192d128_bf16", [(0, 0), (7, 9), (15, 15)]),
-    ("causal_window1024_b2h32n16384d64_bf16", [(0, 0), (1, 31)]),
+    ("noncausal_b16h16n8192d128_bf16", SPREAD_16 + [(0, 0), (15, 15)]),
 ])
 def test_workload_full_size_sampled(lib, name, heads):
     w = BY_NAME[name]
@@ -208,6 +210,26 @@ def test_workload_full_size_sampled(lib, name, heads):
     o, lse = o.cpu(), lse.cpu()
     del q, k, v
     check_workload_heads(o, lse, w, heads, 384)
+
+
+def test_workload_sliding_window_full_compare(lib):
+    """Causal window 1024, B2 H32 N16384 d64: every head and every row against
+    the banded fp64 oracle (each row's 1025 allowed keys)."""
+    w = BY_NAME["causal_window1024_b2h32n16384d64_bf16"]
+    q, k, v = workload_qkv(w, device="cuda")
+    o, lse = lib.fwd(q, k, v, causal=w.causal, window=w.window, scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    del q, k, v
+    worst = [0.0, 0.0, 0.0]
+    for b in range(w.B):
+        for h in range(w.H):
+            qh, kh, vh = workload_head(w, b, h)
+            ref_o, ref_lse = attention_rows(qh, kh, vh, w.scale, w.causal, w.window)
+            r = check_bf16(o[b, h], lse[b, h], ref_o, ref_lse, f"{w.name} head {(b, h)}")
+            worst = [max(a, b_) for a, b_ in zip(worst, r)]
+    print(f"{w.name}: all {w.B * w.H} heads, all rows: max_abs {worst[0]:.2e} "
+          f"l1_rel {worst[1]:.2e} lse {worst[2]:.2e}")
 
 
 # ----------------------------------------------------------------- fp8
@@ -236,6 +258,49 @@ def test_quantize_zero_block_and_saturation_edge(lib):
     rc, rds = o_quantize(x)
     assert np.array_equal(x8.cpu().numpy(), rc) and np.array_equal(ds.cpu().numpy(), rds)
     assert ds[0, 0, 0].item() == 1.0 and (x8[0, 0, :128] == 0).all()
+
+
+def _tiny_blocks(d, seed):
+    """Blocks of 128 rows whose amax is 1e-37, 3e-36, 448 * 2^-126 exactly, a
+    bf16 subnormal (2^-130), 1 and 0, each with some exact zeros: the
+    quantiser's rule for amax / 448 below the smallest normal fp32."""
+    g = torch.Generator().manual_seed(seed)
+    blocks = []
+    for amax in (1e-37, 3e-36, 7 * 2.0 ** -120, 2.0 ** -130, 1.0, 0.0):
+        x = (torch.rand(128, d, generator=g, dtype=torch.float64) * 2 - 1) * amax
+        x[0, 0] = amax
+        x[5, :7] = 0.0
+        blocks.append(x)
+    return torch.cat(blocks).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_quantize_tiny_blocks_bit_exact(lib, d, per_tensor):
+    x = _tiny_blocks(d, 41 + d)[None, None]
+    if per_tensor:
+        x = x[:, :, :512]     # global amax 1e-37 .. 448 * 2^-126: the tiny rule in every slot
+    x8, ds = lib.quantize(x.cuda(), per_tensor=per_tensor)
+    torch.cuda.synchronize()
+    rc, rds = o_quantize(x, per_tensor=per_tensor)
+    assert np.array_equal(x8.cpu().numpy(), rc)
+    assert np.array_equal(ds.cpu().numpy(), rds)
+    assert (ds.cpu() >= 2.0 ** -126).all()
+    assert not (x8.cpu() == 0x7F).any() and not (x8.cpu() == 0xFF).any()
+
+
+def test_fp8_tiny_v_blocks(lib):
+    """V blocks quantised under the tiny rule (descale 2^-126, the smallest
+    normal fp32): the V descale's power of two reaches the bottom of the E8M0
+    range, and O stays within the P-rounding bound of the dequantised oracle."""
+    N, d = 768, 128
+    q, k, _ = make_qkv(1, 2, N, d, seed=42)
+    v = torch.stack([_tiny_blocks(d, 43), _tiny_blocks(d, 44)])[None]
+    scale = 1 / math.sqrt(d)
+    for causal in (False, True):
+        o, lse, codes = fp8_run(lib, q, k, v, False, causal, -1, scale)
+        assert float(codes[5].min()) == 2.0 ** -126   # the V descales include the tiny rule's
+        check_fp8_vs_dequantised(o, lse, codes, scale, causal, -1, f"tiny V causal={causal}", False)
 
 
 def fp8_run(lib, q, k, v, per_tensor, causal=False, window=-1, scale=None):
@@ -316,7 +381,8 @@ def check_fp8_vs_dequantised(o, lse, codes, scale, causal, window, what, outlier
 
 
 @pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 64), (1, 2, 127, 128), (1, 1, 256, 64), (2, 2, 300, 128),
-                                     (1, 1, 1000, 128)])
+                                     (1, 1, 1000, 128), (1, 1, 333, 64), (2, 3, 1000, 64),
+                                     (1, 1, 4097, 64)])
 @pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 100), (False, 70)])
 @pytest.mark.parametrize("outliers", [False, True])
 def test_fp8_vs_dequantised_oracle(lib, B, H, N, d, causal, window, outliers):
@@ -327,12 +393,13 @@ def test_fp8_vs_dequantised_oracle(lib, B, H, N, d, causal, window, outliers):
                              f"{(B, H, N, d, causal, window, outliers)}", outliers)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N,causal", [(300, False), (300, True), (513, True)])
-def test_fp8_wide_grid(lib, N, causal):
+def test_fp8_wide_grid(lib, d, N, causal):
     # a large grid (B32 H32) with ragged N, checked on sampled heads against
     # the bound above
-    B, H, d = 32, 32, 128
-    q, k, v = make_qkv(B, H, N, d, seed=60 + N)
+    B, H = 32, 32
+    q, k, v = make_qkv(B, H, N, d, seed=60 + N + d)
     scale = 1 / math.sqrt(d)
     o, lse, codes = fp8_run(lib, q, k, v, False, causal, -1, scale)
     for b, h in ((0, 0), (9, 30), (31, 31)):
@@ -348,13 +415,14 @@ def test_fp8_scales(lib, scale):
     check_fp8_vs_dequantised(o, lse, codes, scale, True, -1, f"scale={scale}", False)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_running_max_grows_past_rebase(lib, causal):
+def test_fp8_running_max_grows_past_rebase(lib, d, causal):
     """Scores that rise along the keys (key j aligned with every query, with
     weight ~ j), so a row's running max climbs by ~130 log2 units over the
     row: past the 64-unit shift the kernel applies through the PV scale, so
     O and l are rebased on the way."""
-    N, d = 1024, 128
+    N = 1024
     g = torch.Generator().manual_seed(71)
     e = torch.randn(d, generator=g, dtype=torch.float64)
     e /= e.norm()
@@ -392,12 +460,13 @@ def test_bf16_max_n_window(lib, d, N):
     del q, k, v, o, lse
 
 
-def test_fp8_max_n_window(lib):
-    """All-E4M3 attention at N = ATTN_MAX_N, d = 128, causal window 1024:
-    the quantiser and the fp8 kernel at their largest offsets. Sampled rows
-    inside the P-rounding bound of the oracle on the dequantised band."""
-    N, d, w = 1 << 23, 128, 1024
-    g = torch.Generator(device="cuda").manual_seed(95)
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_max_n_window(lib, d):
+    """All-E4M3 attention at N = ATTN_MAX_N, causal window 1024: the quantiser
+    and the fp8 kernel at their largest offsets. Sampled rows inside the
+    P-rounding bound of the oracle on the dequantised band."""
+    N, w = 1 << 23, 1024
+    g = torch.Generator(device="cuda").manual_seed(95 + d)
     x = [torch.randn((1, 1, N, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3)]
     (q8, dq), (k8, dk), (v8, dv) = [lib.quantize(t) for t in x]
     del x
@@ -461,6 +530,9 @@ def test_fp8_v_blocks_far_apart(lib, zero_block):
                                  f"v blocks apart causal={causal} zero={zero_block}", False)
 
 
+SPREAD_8x16 = [(i % 8, (5 * i + 1) % 16) for i in range(16)]   # 16 heads, each batch twice
+
+
 def test_fp8_outlier_workload_full_size(lib):
     """B8 H16 N8192 d128 with x10 outlier channels, per-block and per-tensor.
 
@@ -478,7 +550,7 @@ def test_fp8_outlier_workload_full_size(lib):
         del q8, k8, v8, o, lse
     del q, k, v
     errs = {False: [], True: []}
-    for (b, h) in [(0, 0), (3, 11), (7, 15)]:
+    for (b, h) in SPREAD_8x16:
         qh, kh, vh = workload_head(w, b, h)
         rows = sampled_rows(w.N, 256, 300 + b * 31 + h)
         ref_o, _ = attention_rows(qh, kh, vh, w.scale, False, -1, rows)
@@ -565,7 +637,7 @@ def test_fp8pv_outlier_workload_meets_the_bar(lib):
     del q, k, v, v8, q8, k8
     num = {"pv": 0.0, "all": 0.0}
     den = 0.0
-    for (b, h) in [(0, 0), (2, 5), (5, 9), (7, 15)]:
+    for (b, h) in SPREAD_8x16:
         qh, kh, vh = workload_head(w, b, h)
         rows = sampled_rows(w.N, 256, 500 + b * 31 + h)
         ref_o, _ = attention_rows(qh, kh, vh, w.scale, False, -1, rows)
