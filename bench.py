@@ -1,27 +1,26 @@
 """Attention forward throughput on one MI355X, one JSON line on stdout.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--no-fp8] [--no-merge] [--no-decode]
-                    [--no-d256]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-fp8] [--no-configs] [--no-merge] [--no-decode] [--no-d256]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-  bf16: one attn_fwd launch over B16 H16 N8192 d128 (non-causal);
-  fp8:  attn_fp8_quantize of Q, K and V (per 128-row block) plus one fp8
-        attn_fwd launch over the same shape (x10 outlier channels); the fp8
-        PV mode (bf16 scores, E4M3 P and V) is timed beside it.
-The LSE merge of 4 fp32 partials of the bf16 shape ("lse_merge"), a decode
-step (one query per sequence against a 16K-token cache, "decode") and the
-same step against a paged cache ("decode_paged") are timed
-as their own objects, each against the HBM roofline.
-Inputs are generated by attn_inputs and are resident in HBM before timing.
+one bf16 attn_fwd launch over B16 H16 N8192 d128 (non-causal), the headline
+workload; `value`, `ms_per_step` and `roofline` are that launch's.
+Beside it, each in its own object:
+  "configs": the other bf16 workloads (B1 H2 N256 d64; causal B4 H16 N2048
+             d128; causal window 1024 B2 H32 N16384 d64), each timed with HIP
+             events on the launch stream, with its roofline and its accuracy
+             against the fp64 oracle on sampled heads;
+  "fp8":     the x10-outlier workload at B8 (its configured batch) and at B16
+             (the headline shape): attn_fp8_quantize of Q, K, V (per 128-row
+             block, and per tensor: the naive baseline) plus the all-E4M3
+             attn_fwd; the fp8 PV mode (bf16 scores, E4M3 P and V); RMSE/RMS
+             against the unquantised fp64 oracle for each mode;
+  "lse_merge", "decode", "decode_paged", "d256": the next-row kernels.
+Inputs come from attn_inputs and are resident in HBM before timing.
 TFLOP/s counts algorithmic FLOP: 4 * d * (number of allowed query/key pairs).
-
-`value` is the bf16 throughput; the fp8 figures sit under "fp8". "roofline"
-reports the dominant kernel (bf16 attention) against the dense bf16 MFMA peak,
-with its per-launch duration measured by HIP events on the launch stream;
-"fp8" carries the same object for the all-E4M3 kernel against the fp8 peak.
-"cpu_baseline" times the fp64 oracle on a bounded sample of heads of the same
-workload on the host cores (rank 0, N=1 only) and reports parity on them.
+"cpu_baseline" times the fp64 oracle on a bounded sample of heads of the
+headline workload on the host cores (rank 0, N=1 only).
 """
 from __future__ import annotations
 
@@ -40,6 +39,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
 PEAK_FP8_TFLOPS = 5033.2       # dense fp8
 PEAK_HBM_GBS = 8000.0
+# fp8 PV mode: half the FLOPs on bf16 MFMAs (QK^T), half on fp8 (PV)
+PEAK_MIXED_TFLOPS = 1.0 / (0.5 / PEAK_BF16_TFLOPS + 0.5 / PEAK_FP8_TFLOPS)
 METRIC = "attn fwd TFLOP/s and % MFMA peak, B16 H16 N8192 d128, bf16 and fp8"
 DEFAULT_WORKLOAD = "noncausal_b16h16n8192d128_bf16"
 FP8_WORKLOAD = "noncausal_b8h16n8192d128_fp8_outliers"
@@ -139,14 +140,208 @@ def cpu_baseline(w, o_gpu, lse_gpu, budget_s: float = 15.0):
     }
 
 
+def time_grouped(fn, groups: int, per_group: int, warmup: int, stream):
+    """Per-launch ms of back-to-back launches: `groups` groups of `per_group`
+    launches, each group between one pair of HIP events on the launch stream;
+    returns the per-launch time of every group. For launches of tens of
+    microseconds an event pair around each one would add its own gaps."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(groups):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(per_group):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / per_group)
+    return out
+
+
+def workload_flop(w, B=None) -> float:
+    return 4.0 * w.d * allowed_pairs(w.N, w.causal, w.window) * (w.B if B is None else B) * w.H
+
+
+def mean_ms(ev):
+    return sum(ev) / len(ev)
+
+
+def spread_heads(B, H, count):
+    """`count` distinct (b, h) pairs spread over batches and heads."""
+    out = []
+    for i in range(B * H):
+        b, h = i % B, (5 * i + i // B) % H
+        if (b, h) not in out:
+            out.append((b, h))
+        if len(out) == count:
+            break
+    return out
+
+
+def bf16_accuracy(w, samples):
+    """Worst max-abs, L1-rel and LSE error over the sampled whole heads
+    (oracle leg: runs only with the CPU baseline)."""
+    from attn_inputs import workload_head
+    from oracle import attention_rows, max_abs, l1_rel
+    worst = {"max_abs": 0.0, "l1_rel": 0.0, "lse_max_abs": 0.0}
+    for (b, h), (ob, lb) in samples.items():
+        q, k, v = workload_head(w, b, h)
+        ref_o, ref_lse = attention_rows(q, k, v, w.scale, w.causal, w.window)
+        worst["max_abs"] = max(worst["max_abs"], max_abs(ob, ref_o))
+        worst["l1_rel"] = max(worst["l1_rel"], l1_rel(ob, ref_o))
+        worst["lse_max_abs"] = max(worst["lse_max_abs"], max_abs(lb, ref_lse))
+    worst["sample"] = f"{len(samples)} whole heads ({w.N} rows each)"
+    worst["meets_bar"] = worst["max_abs"] <= 2e-2 and worst["l1_rel"] <= 5e-3
+    return worst
+
+
+def bench_bf16_config(tafa, w, dev, steps, warmup, stream):
+    """One bf16 workload: time, TFLOP/s and roofline. Returns the entry and the
+    outputs of a few whole heads (host copies) for the oracle leg."""
+    import torch
+    from attn_inputs import workload_qkv
+    q, k, v = workload_qkv(w, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    run = lambda: tafa.fwd(q, k, v, causal=w.causal, window=w.window, scale=w.scale, out=o, lse=lse)
+    # launches shorter than ~1 ms: groups of back-to-back launches, median group
+    groups, per_group = 9, 50
+    per_launch = sorted(time_grouped(run, groups, per_group, max(warmup, 20), stream))
+    ms = per_launch[groups // 2]
+    n = groups * per_group
+    flop = workload_flop(w)
+    tf = flop / (ms * 1e-3) / 1e12
+    samples = {(b, h): (o[b, h].cpu(), lse[b, h].cpu()) for b, h in spread_heads(w.B, w.H, 4)}
+    del q, k, v, o, lse
+    entry = {
+        "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+        "window": w.window, "dtype": "bf16", "launches_timed": n,
+        "timing": f"median of {groups} groups of {per_group} back-to-back launches, HIP events",
+        "avg_launch_ms": round(ms, 5),
+        "tflops": round(tf, 2), "algorithmic_tflop": flop / 1e12,
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    return entry, samples
+
+
+def fp8_accuracy(w, outs, heads, rows):
+    """RMSE/RMS of each mode's sampled output against the unquantised fp64
+    oracle, pooled over the sampled rows of the sampled heads (oracle leg)."""
+    from attn_inputs import workload_head
+    from oracle import attention_rows
+    num = {m: 0.0 for m in outs}
+    den = 0.0
+    for i, (b, h) in enumerate(heads):
+        q, k, v = workload_head(w, b, h)
+        ref_o, _ = attention_rows(q, k, v, w.scale, w.causal, w.window, rows)
+        den += float(ref_o.pow(2).sum())
+        for m, o in outs.items():
+            num[m] += float((o[i].double() - ref_o).pow(2).sum())
+    acc = {m: round(math.sqrt(num[m] / den), 5) for m in outs}
+    return {"rmse_rel": acc, "meets_bar": {m: acc[m] <= 3e-2 for m in outs},
+            "beats_per_tensor": {m: acc[m] < acc["per_tensor_naive"] for m in outs
+                                 if m != "per_tensor_naive"},
+            "sample": f"{len(heads)} heads x {len(rows)} rows"}
+
+
+def bench_fp8(tafa, dev, steps, warmup, stream):
+    """The x10-outlier workload: all-E4M3 (per block and per tensor) and the fp8
+    PV mode, at B8 (accuracy and speed) and B16 (speed, the headline shape)."""
+    import torch
+    from attn_inputs import BY_NAME, workload_qkv
+    wf = BY_NAME[FP8_WORKLOAD]
+    res = {"workload": wf.name, "dtype": "fp8_e4m3", "accuracy_bar_rmse_rel": 3e-2}
+    for B in (wf.B, 16):
+        print(f"[bench] fp8: generating {wf.name} at B={B}", file=sys.stderr, flush=True)
+        q, k, v = workload_qkv(wf, device=dev, B=B)
+        bufs = {name: tafa.quantize(t) for name, t in (("q", q), ("k", k), ("v", v))}
+        o = torch.empty_like(q)
+        lse = torch.empty((B, wf.H, wf.N), dtype=torch.float32, device=dev)
+        flop = workload_flop(wf, B)
+
+        def quant(per_tensor=False):
+            for name, t in (("q", q), ("k", k), ("v", v)):
+                tafa.quantize(t, per_tensor=per_tensor, out=bufs[name][0], descale=bufs[name][1])
+
+        def attn8():
+            tafa.fwd(bufs["q"][0], bufs["k"][0], bufs["v"][0], scale=wf.scale,
+                     descales=(bufs["q"][1], bufs["k"][1], bufs["v"][1]), out=o, lse=lse)
+
+        def attn_pv():
+            tafa.fwd(q, k, bufs["v"][0], scale=wf.scale, descales=(None, None, bufs["v"][1]),
+                     out=o, lse=lse)
+
+        def step8():
+            quant()
+            attn8()
+
+        print(f"[bench] fp8: timing at B={B}", file=sys.stderr, flush=True)
+        quant()
+        _, ev_a = time_launches(attn8, steps, warmup, stream)
+        _, ev_q = time_launches(quant, steps, warmup, stream)
+        wall8, _ = time_launches(step8, steps, warmup, stream)
+        _, ev_pv = time_launches(attn_pv, max(1, steps // 2), warmup, stream)
+        a_ms, q_ms, pv_ms = mean_ms(ev_a), mean_ms(ev_q), mean_ms(ev_pv)
+        qbytes = 3 * q.numel() * (2 + 1) + 3 * bufs["q"][1].numel() * 4
+        a_tf, pv_tf = flop / (a_ms * 1e-3) / 1e12, flop / (pv_ms * 1e-3) / 1e12
+        entry = {
+            "B": B, "H": wf.H, "N": wf.N, "d": wf.d, "algorithmic_tflop": flop / 1e12,
+            "all_e4m3": {
+                "avg_launch_ms": round(a_ms, 4), "tflops": round(a_tf, 2),
+                "frac_of_dense_fp8_peak": round(a_tf / PEAK_FP8_TFLOPS, 4),
+                "quantize_qkv_ms": round(q_ms, 4),
+                "quantize_gbs": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+                "quantize_frac_of_hbm_peak": round(qbytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "end_to_end_ms_per_step": round(wall8, 4),
+                "end_to_end_tflops": round(flop / (wall8 * 1e-3) / 1e12, 2)},
+            "pv_mode": {
+                "what": "bf16 Q, K (scores on bf16 MFMAs); E4M3 V and P (PV on fp8 MFMAs)",
+                "avg_launch_ms": round(pv_ms, 4), "tflops": round(pv_tf, 2),
+                "frac_of_dense_fp8_peak": round(pv_tf / PEAK_FP8_TFLOPS, 4),
+                "frac_of_mixed_ceiling": round(pv_tf / PEAK_MIXED_TFLOPS, 4),
+                "mixed_ceiling_tflops": round(PEAK_MIXED_TFLOPS, 1)},
+        }
+        if B == wf.B:
+            # sampled outputs of each mode, for the oracle leg's RMSE/RMS
+            heads = spread_heads(B, wf.H, 8)
+            rows = sorted(set(range(0, wf.N, 64)) | {wf.N - 1})
+            hi = torch.tensor([b * wf.H + h for b, h in heads], device=dev)
+            ri = torch.tensor(rows, device=dev)
+            take = lambda t: t.view(B * wf.H, wf.N, wf.d)[hi][:, ri].cpu()
+            outs = {}
+            attn8()
+            outs["per_block"] = take(o)
+            attn_pv()
+            outs["pv_mode"] = take(o)
+            quant(per_tensor=True)
+            attn8()
+            outs["per_tensor_naive"] = take(o)
+            quant()
+            res["_samples"] = (wf, outs, heads, rows)
+        res[f"B{B}"] = entry
+        del q, k, v, bufs, o, lse
+        torch.cuda.empty_cache()
+    b16 = res["B16"]["all_e4m3"]
+    res["roofline"] = {"bound": "mfma", "kernel": "attn_fwd_fp8_kernel<128, false>",
+                       "achieved": b16["tflops"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                       "frac": b16["frac_of_dense_fp8_peak"],
+                       "traffic": recorded_traffic("noncausal_b16h16n8192d128_fp8", "fp8"),
+                       "avg_launch_ms": b16["avg_launch_ms"]}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-d256", action="store_true")
@@ -171,13 +366,13 @@ def main():
                           "copy_bytes_written_per_launch": dst.numel() * 2}))
         return
     import tiled_attention_forward_attn_amd as tafa
-    from attn_inputs import BY_NAME, workload_qkv
+    from attn_inputs import BY_NAME, WORKLOADS, workload_qkv
     tafa.load()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
-    w = BY_NAME[args.workload]
-    flop = 4.0 * w.d * allowed_pairs(w.N, w.causal, w.window) * w.B * w.H
+    w = BY_NAME[DEFAULT_WORKLOAD]
+    flop = workload_flop(w)
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     q, k, v = workload_qkv(w, device=dev)
     o = torch.empty_like(q)
@@ -186,10 +381,13 @@ def main():
           file=sys.stderr, flush=True)
     run = lambda: tafa.fwd(q, k, v, causal=w.causal, window=w.window, scale=w.scale, out=o, lse=lse)
     wall_ms, ev = time_launches(run, args.steps, args.warmup, stream)
-    kern_ms = sum(ev) / len(ev)
+    kern_ms = mean_ms(ev)
     tflops = flop / (wall_ms * 1e-3) / 1e12
     achieved = flop / (kern_ms * 1e-3) / 1e12
     traffic = recorded_traffic(w.name, "bf16")
+    o_host, lse_host = o.cpu(), lse.cpu()
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
 
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -200,75 +398,29 @@ def main():
                    "causal": w.causal, "window": w.window, "scale": w.scale,
                    "algorithmic_tflop_per_step": flop / 1e12},
         "frac_of_dense_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<128>",
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<128, 32, 1, 8, false>",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(kern_ms, 4)},
     }
 
-    if not args.no_fp8 and w.name == DEFAULT_WORKLOAD:
-        wf = BY_NAME[FP8_WORKLOAD]
-        B16 = w.B
-        print(f"[bench] generating {wf.name} at B={B16}", file=sys.stderr, flush=True)
-        qf, kf, vf = workload_qkv(wf, device=dev, B=B16)
-        bufs = {}
-        for name, t in (("q", qf), ("k", kf), ("v", vf)):
-            bufs[name] = tafa.quantize(t)
-        torch.cuda.synchronize()
-        of = torch.empty_like(qf)
-        lf = torch.empty((B16, wf.H, wf.N), dtype=torch.float32, device=dev)
-        flop8 = 4.0 * wf.d * wf.N * wf.N * B16 * wf.H
+    oracle_work = []   # (object, workload, sampled outputs) for the oracle leg
+    if not args.no_configs:
+        line["configs"] = {}
+        for wc in WORKLOADS:
+            if wc.name == DEFAULT_WORKLOAD or wc.dtype != "bf16":
+                continue
+            print(f"[bench] timing {wc.name}", file=sys.stderr, flush=True)
+            entry, samples = bench_bf16_config(tafa, wc, dev, args.steps, args.warmup, stream)
+            line["configs"][wc.name] = entry
+            oracle_work.append((entry, wc, samples))
+            torch.cuda.empty_cache()
 
-        def quant():
-            for name, t in (("q", qf), ("k", kf), ("v", vf)):
-                tafa.quantize(t, out=bufs[name][0], descale=bufs[name][1])
+    if not args.no_fp8:
+        line["fp8"] = bench_fp8(tafa, dev, args.steps, args.warmup, stream)
+        fp8_samples = line["fp8"].pop("_samples")
 
-        def attn8():
-            tafa.fwd(bufs["q"][0], bufs["k"][0], bufs["v"][0], scale=wf.scale,
-                     descales=(bufs["q"][1], bufs["k"][1], bufs["v"][1]), out=of, lse=lf)
-
-        def step8():
-            quant()
-            attn8()
-
-        def attn_pv():
-            tafa.fwd(qf, kf, bufs["v"][0], scale=wf.scale, descales=(None, None, bufs["v"][1]),
-                     out=of, lse=lf)
-
-        print("[bench] timing fp8 quantise + attention", file=sys.stderr, flush=True)
-        _, ev_a = time_launches(attn8, args.steps, args.warmup, stream)
-        _, ev_q = time_launches(quant, args.steps, args.warmup, stream)
-        wall8, _ = time_launches(step8, args.steps, args.warmup, stream)
-        _, ev_pv = time_launches(attn_pv, max(1, args.steps // 2), args.warmup, stream)
-        a_ms = sum(ev_a) / len(ev_a)
-        q_ms = sum(ev_q) / len(ev_q)
-        pv_ms = sum(ev_pv) / len(ev_pv)
-        qbytes = 3 * qf.numel() * (2 + 1) + 3 * bufs["q"][1].numel() * 4
-        line["fp8"] = {
-            "workload": f"{wf.name} at B={B16}", "dtype": "fp8_e4m3",
-            "attention_tflops": round(flop8 / (a_ms * 1e-3) / 1e12, 2),
-            "attention_frac_of_dense_fp8_peak": round(flop8 / (a_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
-            "attention_avg_launch_ms": round(a_ms, 4),
-            "quantize_qkv_ms": round(q_ms, 4),
-            "quantize_gbs": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
-            "quantize_frac_of_hbm_peak": round(qbytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "end_to_end_ms_per_step": round(wall8, 4),
-            "end_to_end_tflops": round(flop8 / (wall8 * 1e-3) / 1e12, 2),
-            # dtype 2: scores on bf16 MFMAs from bf16 Q, K; P and V in E4M3
-            "pv_mode_attention_tflops": round(flop8 / (pv_ms * 1e-3) / 1e12, 2),
-            "pv_mode_attention_avg_launch_ms": round(pv_ms, 4),
-            # the all-E4M3 attention kernel against the dense fp8 MFMA peak;
-            # traffic: profiled HBM bytes per launch on the current sources
-            "roofline": {"bound": "mfma", "kernel": "attn_fwd_fp8_kernel<128, false>",
-                         "achieved": round(flop8 / (a_ms * 1e-3) / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
-                         "unit": "TFLOP/s",
-                         "frac": round(flop8 / (a_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
-                         "traffic": recorded_traffic("noncausal_b16h16n8192d128_fp8", "fp8"),
-                         "avg_launch_ms": round(a_ms, 4)},
-        }
-        del qf, kf, vf, of, lf, bufs
-
-    if not args.no_d256 and w.name == DEFAULT_WORKLOAD:
+    if not args.no_d256:
         # head dimension 256: B8 H16 N8192 (the FLOPs of the headline shape)
         Bh, Hh, Nh, dh = 8, 16, 8192, 256
         print(f"[bench] timing bf16 attention B{Bh} H{Hh} N{Nh} d{dh}", file=sys.stderr, flush=True)
@@ -287,7 +439,7 @@ def main():
                         "avg_launch_ms": round(h_ms, 4)}
         del q2, k2, v2, o2, l2
 
-    if not args.no_merge and w.name == DEFAULT_WORKLOAD:
+    if not args.no_merge:
         # attn_lse_merge of R = 4 fp32 partials of the headline shape (the
         # combination a 4-way split of the keys needs): HBM-bound
         R = 4
@@ -311,7 +463,7 @@ def main():
         }
         del o_p, l_p, om, lm
 
-    if not args.no_decode and w.name == DEFAULT_WORKLOAD:
+    if not args.no_decode:
         # attn_decode: one new query per sequence against a 16K-token cache
         Bd, Hd, Nq, Nk, dd = 32, 32, 1, 16384, 128
         print(f"[bench] timing attn_decode B{Bd} H{Hd} Nq{Nq} Nk{Nk} d{dd}", file=sys.stderr, flush=True)
@@ -365,8 +517,16 @@ def main():
         del qd, kc, vc, table, lens, ws, od, ld
 
     if not args.no_cpu_baseline:
+        # the oracle leg: the fp64 oracle timed on host cores, and the accuracy
+        # of every timed workload's sampled outputs against it
         print("[bench] timing the fp64 oracle on host cores", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, o.cpu(), lse.cpu())
+        line["cpu_baseline"] = cpu_baseline(w, o_host, lse_host)
+        for entry, wc, samples in oracle_work:
+            print(f"[bench] oracle: accuracy of {wc.name}", file=sys.stderr, flush=True)
+            entry["accuracy_vs_fp64_oracle"] = bf16_accuracy(wc, samples)
+        if not args.no_fp8:
+            print("[bench] oracle: fp8 RMSE/RMS per mode", file=sys.stderr, flush=True)
+            line["fp8"]["B8"]["accuracy_vs_unquantised_fp64_oracle"] = fp8_accuracy(*fp8_samples)
     print(json.dumps(line), flush=True)
 
 

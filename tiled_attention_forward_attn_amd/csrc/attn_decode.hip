@@ -52,8 +52,7 @@ struct DecodeWave {
   lds_char* vl[2];
   int Nq, Nk, causal, k_hi, lane, h, l32, qrow;
   float c;
-  i32x4 kres, vres;   // contiguous cache: descriptors over this head's K and V
-  uint32_t kvbytes;   // their size, Nk D 2
+  i32x4 kres, vres;
   int koff[LOADS], voff[LOADS];
   // paged cache: pool base, this sequence's block table row (read through the
   // constant address space, so a scalar load that the copies' vmcnt waits do
@@ -111,7 +110,7 @@ struct DecodeWave {
         return;
       }
     }
-    i32x4 kr, vr;
+    int soff = (int)((uint32_t)t * TILE);
     if constexpr (PAGED) {
       // descriptors over tile t's rows of its page; zero rows past k_hi
       uint32_t bytes = 0;
@@ -128,17 +127,14 @@ struct DecodeWave {
           bytes = (uint32_t)min(BN, k_hi - p0) * D * 2;
         }
       }
-      kr = make_rsrc(kb, bytes);
-      vr = make_rsrc(vb, bytes);
-    } else {
-      // tile t's rows of this head; zero rows past Nk
-      kr = rsrc_from(kres, kvbytes, (uint32_t)t * TILE);
-      vr = rsrc_from(vres, kvbytes, (uint32_t)t * TILE);
+      kres = make_rsrc(kb, bytes);
+      vres = make_rsrc(vb, bytes);
+      soff = 0;
     }
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      copy_to_lds16(kr, kl[ST] + u * 1024, koff[u]);
-      copy_to_lds16(vr, vl[ST] + u * 1024, voff[u]);
+      copy_to_lds16(kres, kl[ST] + u * 1024, koff[u], soff);
+      copy_to_lds16(vres, vl[ST] + u * 1024, voff[u], soff);
     }
   }
 
@@ -292,9 +288,8 @@ void attn_decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
   if (k_lo < st.k_hi) {
     if constexpr (!PAGED) {
-      st.kvbytes = (uint32_t)Nk * D * 2;
-      st.kres = make_rsrc(K + khead, st.kvbytes);
-      st.vres = make_rsrc(V + khead, st.kvbytes);
+      st.kres = make_rsrc(K + khead, (uint32_t)Nk * D * 2);
+      st.vres = make_rsrc(V + khead, (uint32_t)Nk * D * 2);
       st.kg = K + khead;
       st.vg = V + khead;
     }

@@ -39,35 +39,25 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   return i32x4{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffff), (int)bytes, kRsrcWord3};
 }
 // 16-byte HBM -> LDS copy of one lane's chunk (buffer_load_dwordx4 ... lds):
-// the wave's 64 chunks land contiguously at lds_base + 16 * lane. `offset` is
-// the chunk's whole byte offset from the descriptor's base. It travels in the
-// VGPR offset, the part of the address the buffer range check covers (the
-// scalar offset is added after the check), and the scalar offset is 0: a
-// chunk at or past the descriptor's size reads as zero and touches no memory.
+// the wave's 64 chunks land contiguously at lds_base + 16 * lane, read from
+// the descriptor's base + soffset + voffset. On gfx950 the buffer range check
+// compares the whole offset, soffset + voffset, with the descriptor's size
+// (measured: a descriptor sized to size - soffset zeroes every chunk at
+// soffset + voffset >= size - soffset, and chunks past a head's end read as
+// zero with NaN-filled memory right behind it). So the kernels put a tile's
+// offset in soffset over a descriptor of the whole head, and a chunk at or
+// past the head's end reads as zero and touches no memory.
 // Issued from inline assembly, so the compiler does not track its LDS write:
 // the callers order it with explicit vmcnt waits and barriers. (The compiler
 // cannot tell that the transposing LDS reads of one tile never touch the tile
 // still being copied, and would otherwise wait for every copy in flight
 // before each of them.) M0 carries the LDS address.
-__device__ __forceinline__ void copy_to_lds16(i32x4 rsrc, const lds_char* lds_base, uint32_t offset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+__device__ __forceinline__ void copy_to_lds16(i32x4 rsrc, const lds_char* lds_base, int voffset,
+                                              int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"((uint32_t)(uintptr_t)lds_base), "v"(offset), "s"(rsrc)
+               : "s"((uint32_t)(uintptr_t)lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
                : "memory", "m0");
-}
-// Descriptor over the bytes [off, total) of the range that `rsrc` covers
-// (total bytes from its base): base moved by off, size total - off, or 0 once
-// off reaches total. A copy through it at VGPR offset x reads byte off + x of
-// the range, or zero when that lies at or past total. Callers pass
-// wave-uniform multiples of 16 below 2^32, so this is a few scalar
-// instructions: the size is a signed max in 16-byte units (the scalar unit has
-// a signed max; the units keep both operands below 2^28, so nothing wraps).
-__device__ __forceinline__ i32x4 rsrc_from(i32x4 rsrc, uint32_t total, uint32_t off) {
-  const unsigned long long a =
-      (((unsigned long long)(uint32_t)rsrc[1] & 0xffff) << 32 | (uint32_t)rsrc[0]) + off;
-  const uint32_t hi = ((uint32_t)rsrc[1] & 0xffff0000u) | (uint32_t)((a >> 32) & 0xffff);
-  const int n16 = max((int)(total >> 4) - (int)(off >> 4), 0);
-  return i32x4{(int)(uint32_t)a, (int)hi, (int)((uint32_t)n16 << 4), rsrc[3]};
 }
 // The same 16-byte HBM -> LDS copy from a flat global address, marked
 // nontemporal (streamed data: gfx950 accepts the nt bit on this form, not on

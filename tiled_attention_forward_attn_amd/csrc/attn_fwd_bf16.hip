@@ -80,7 +80,6 @@ struct Bf16Fwd {
   int lane, wave, h, l32;
   int qrow[QB];
   i32x4 kres, vres;                  // buffer descriptors of this head's K and V
-  uint32_t kvbytes;                  // their size, N D 2
   int koff[LOADS], voff[LOADS];
   // state
   bf16x8 qf[QB][KSTEPS];
@@ -96,13 +95,13 @@ struct Bf16Fwd {
   __device__ __forceinline__ void issue_k(int kt) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
-      copy_to_lds16(rsrc_from(kres, kvbytes, (uint32_t)kt * TILE), kl[ST] + (u * NW + wave) * 1024, koff[u]);
+      copy_to_lds16(kres, kl[ST] + (u * NW + wave) * 1024, koff[u], (int)((uint32_t)kt * (BN * D * 2)));
   }
   template <int ST>
   __device__ __forceinline__ void issue_v(int kt) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
-      copy_to_lds16(rsrc_from(vres, kvbytes, (uint32_t)kt * TILE), vl[ST] + (u * NW + wave) * 1024, voff[u]);
+      copy_to_lds16(vres, vl[ST] + (u * NW + wave) * 1024, voff[u], (int)((uint32_t)kt * (BN * D * 2)));
   }
 
   // A operand of S^T = K Q^T: lane holds K[32 kb + l32][16 t + 8 h .. +7].
@@ -397,9 +396,8 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         x = (x & qkeep) ^ qsign;  // zero Q for a zero scale; exact sign flip for a negative one
         st.qf[b][t] = __builtin_bit_cast(bf16x8, x);
       }
-    st.kvbytes = (uint32_t)N * D * 2;
-    st.kres = make_rsrc(pk.template get<const uint16_t>() + head, st.kvbytes);
-    st.vres = make_rsrc(pv.template get<const uint16_t>() + head, st.kvbytes);
+    st.kres = make_rsrc(pk.template get<const uint16_t>() + head, (uint32_t)N * D * 2);
+    st.vres = make_rsrc(pv.template get<const uint16_t>() + head, (uint32_t)N * D * 2);
     if (tr.kt0 < tr.kt1) st.template issue_k<0>(tr.kt0);
   };
 

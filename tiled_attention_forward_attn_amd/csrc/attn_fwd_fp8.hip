@@ -117,18 +117,16 @@ struct Fp8Fwd {
   static constexpr int VLOADS = VTILE / (16 * kThreads);
   // Copy round u of a tile lands kThreads / KDCH (or / VDCH) rows below round
   // 0. Both swizzles depend on row bits 0..3 only and the V key order swaps
-  // bits 2 and 3, so round u's HBM offset is round 0's plus u * 16 * kThreads:
-  // one offset register per tensor; the tile's and the round's offsets move
-  // the buffer descriptor (scalar work), so the range check covers them.
+  // bits 2 and 3, so round u's LDS offset is round 0's plus u * 16 * kThreads:
+  // one offset register per tensor, the rest in the scalar offset.
   static_assert((kThreads / KDCH) % 16 == 0 && (kThreads / VDCH) % 16 == 0, "copy rounds");
 
   lds_char* kl[2];
   lds_char* vl[2];
   int N, causal, window, kt0, kt1, qrow;
   int lane, wave, h, l32;
-  i32x4 kres, vres;   // buffer descriptors of this head's K and V
-  uint32_t kbytes, vbytes;   // their sizes
-  int koff, voff;     // byte offset of this lane's copy in round 0 (HBM and LDS image)
+  i32x4 kres, vres;
+  int koff, voff;     // LDS byte offset of this lane's copy in round 0
   int krow, kswz;     // E4M3 K reads: l32 * D and swz_k8(l32) << 4
   const float* dk;
   const float* dv;
@@ -152,15 +150,15 @@ struct Fp8Fwd {
   __device__ __forceinline__ void issue_k(int kt) {
 #pragma unroll
     for (int u = 0; u < KLOADS; ++u)
-      copy_to_lds16(rsrc_from(kres, kbytes, (uint32_t)kt * KTILE + u * 16 * kThreads),
-                    kl[ST] + (u * 4 + wave) * 1024, koff);
+      copy_to_lds16(kres, kl[ST] + (u * 4 + wave) * 1024, koff,
+                    (int)((uint32_t)kt * KTILE + u * 16 * kThreads));
   }
   template <int ST>
   __device__ __forceinline__ void issue_v(int kt) {
 #pragma unroll
     for (int u = 0; u < VLOADS; ++u)
-      copy_to_lds16(rsrc_from(vres, vbytes, (uint32_t)kt * VTILE + u * 16 * kThreads),
-                    vl[ST] + (u * 4 + wave) * 1024, voff);
+      copy_to_lds16(vres, vl[ST] + (u * 4 + wave) * 1024, voff,
+                    (int)((uint32_t)kt * VTILE + u * 16 * kThreads));
   }
 
   // A operand of S^T = K Q^T for 32-key block kb. E4M3: lane holds
@@ -438,10 +436,8 @@ void attn_fwd_fp8_kernel(const void* __restrict__ Qv, const void* __restrict__ K
   // HBM -> LDS copies: LDS chunk p (p = 64 * block + lane) of the K image is
   // row p / KDCH, physical column p % KDCH, holding logical column
   // (p % KDCH) ^ swizzle(row). The V image's LDS row r holds key v8_row(r).
-  st.kbytes = (uint32_t)N * D * S::KBYTES;
-  st.vbytes = (uint32_t)N * D;
-  st.kres = make_rsrc((const char*)Kv + head * S::KBYTES, st.kbytes);
-  st.vres = make_rsrc(V + head, st.vbytes);
+  st.kres = make_rsrc((const char*)Kv + head * S::KBYTES, (uint32_t)N * D * S::KBYTES);
+  st.vres = make_rsrc(V + head, (uint32_t)N * D);
   {
     const int p = st.wave * 64 + st.lane;        // chunk of copy round 0
     const int row = p / S::KDCH, pc = p % S::KDCH;
