@@ -58,7 +58,8 @@ enum {
   ATTN_E_ALIAS = -7,     /* an output overlaps an input or another output             */
   ATTN_E_LAUNCH = -8,    /* the kernel launch failed (no device, bad stream, ...)     */
   ATTN_E_SCALE = -9,     /* scale is not finite                                       */
-  ATTN_E_WORKSPACE = -10 /* decode workspace NULL, misaligned or too small            */
+  ATTN_E_WORKSPACE = -10,/* decode workspace NULL, misaligned or too small            */
+  ATTN_E_SCRATCH = -11   /* attn_decode_noalloc: the call needs more than its scratch */
 };
 
 /* Largest supported sizes (index arithmetic is 64-bit; these bound the grid). */
@@ -202,6 +203,34 @@ size_t attn_decode_workspace_bytes(int B, int H, int Nq, int d, int splits);
 int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int Nq, int Nk, int d, int causal, float scale, int splits,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the static scratch buffer attn_decode_noalloc uses (per device). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16 << 20)
+
+/*
+ * attn_decode_noalloc - attn_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. It computes exactly what attn_decode computes, with the
+ * same kernels, but keeps the fp32 partials and log-sum-exps in a static
+ * buffer of ATTN_NOALLOC_SCRATCH_BYTES bytes that the library holds on every
+ * device it runs on, from the load of its code object until the process
+ * ends. The call allocates and frees nothing.
+ *
+ *   All arguments as in attn_decode, without workspace and workspace_bytes.
+ *   The work uses the buffer of the device `stream` belongs to (the current
+ *   device for the NULL stream).
+ * The buffer needs no clearing (every slot a call reads it has written
+ * first). Calls on one device share that device's buffer: calls that overlap
+ * on one device (different streams or host threads without ordering) race
+ * on it; calls ordered on one stream are safe. Returns ATTN_OK or an ATTN_E_*
+ * code: ATTN_E_SCRATCH when attn_decode_workspace_bytes(B, H, Nq, d, splits)
+ * exceeds ATTN_NOALLOC_SCRATCH_BYTES (nothing is enqueued; fewer splits or a
+ * smaller batch per call fit), ATTN_E_LAUNCH if the buffer's device address
+ * cannot be obtained or the launch fails.
+ */
+int attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Nq, int Nk, int d, int causal, float scale, int splits,
+                        void* stream);
 
 /* Page sizes (positions per page) attn_decode_paged takes: powers of two in
  * this range, so a 32-key tile never spans two pages. */

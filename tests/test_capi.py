@@ -39,15 +39,15 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
     assert set(names) == {"attn_fwd", "attn_fp8_quantize", "attn_lse_merge", "attn_decode",
-                          "attn_decode_workspace_bytes", "attn_decode_paged", "attn_strerror",
-                          "attn_version"}
+                          "attn_decode_workspace_bytes", "attn_decode_paged", "attn_decode_noalloc",
+                          "attn_strerror", "attn_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(tafa.SIGNATURES)
 
 
 def test_version_and_strerror(lib):
-    assert tafa.version() == 10500
+    assert tafa.version() == 10600
     codes = header_codes()
     assert codes["ATTN_OK"] == 0
     texts = {tafa.strerror(c) for c in codes.values()}
@@ -269,3 +269,32 @@ def test_decode_paged_rejects(lib, kw, code):
 def test_decode_paged_empty_problem_is_ok(lib):
     assert call_paged(lib, Nq=0, q=None, ws=None, ws_bytes=0) == E["ATTN_OK"]
     assert call_paged(lib, B=0, table=None, lens=None, ws=None, ws_bytes=0) == E["ATTN_OK"]
+
+
+def call_noalloc(lib, q=A, k=A + GAP, v=A + 2 * GAP, o=A + 3 * GAP, lse=A + 4 * GAP, B=2, H=3, Nq=4,
+                 Nk=1000, d=128, causal=1, scale=0.125, splits=8):
+    return lib.attn_decode_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, splits, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Nq=33), "ATTN_E_SHAPE"), (dict(Nk=3), "ATTN_E_SHAPE"), (dict(splits=0), "ATTN_E_SHAPE"),
+    (dict(B=-1), "ATTN_E_SHAPE"), (dict(d=256), "ATTN_E_HEADDIM"),
+    (dict(q=None), "ATTN_E_NULL"), (dict(lse=None), "ATTN_E_NULL"),
+    (dict(causal=2), "ATTN_E_WINDOW"), (dict(scale=math.nan), "ATTN_E_SCALE"),
+    (dict(k=A + GAP + 8), "ATTN_E_ALIGN"), (dict(o=A + GAP + 4096), "ATTN_E_ALIAS"),
+    # splits * B * H * Nq * (4 d + 4) = 8 * 1024 * 32 * 516 bytes > 16 MiB: refused before any HIP call
+    (dict(B=32, H=32, Nq=32, Nk=4096), "ATTN_E_SCRATCH"),
+])
+def test_decode_noalloc_rejects(lib, kw, code):
+    assert call_noalloc(lib, **kw) == E[code]
+
+
+def test_decode_noalloc_scratch_limit(lib):
+    # the largest call that fits the static buffer is accepted by the checks
+    # (not launched here: the sizes alone decide), one more split is refused
+    limit = 16 << 20
+    assert tafa.NOALLOC_SCRATCH_BYTES == limit
+    need = lib.attn_decode_workspace_bytes(4, 8, 32, 128, 31)      # 31 * 1024 * 516 bytes
+    assert need <= limit < lib.attn_decode_workspace_bytes(4, 8, 32, 128, 32)
+    assert call_noalloc(lib, B=4, H=8, Nq=32, Nk=4096, splits=32) == E["ATTN_E_SCRATCH"]
+    assert call_noalloc(lib, Nq=0, q=None) == E["ATTN_OK"]

@@ -42,6 +42,7 @@ SIGNATURES = {
                          ctypes.c_size_t, _vp]),
     "attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                                _f, _i, _vp, ctypes.c_size_t, _vp]),
+    "attn_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "attn_strerror": (ctypes.c_char_p, [_i]),
     "attn_version": (_i, []),
 }
@@ -284,6 +285,45 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = 
     return out, lse
 
 
+NOALLOC_SCRATCH_BYTES = 16 << 20     # ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                   scale: float | None = None, splits: int | None = None,
+                   out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
+    """decode() through attn_decode_noalloc: the library keeps the partials in
+    its own static device buffer, so the C call allocates nothing (out and lse
+    are allocated here when not given). Calls that overlap on one device race
+    on that buffer."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_4d(name, t)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if splits is None:
+        splits = default_splits(B, H, Nk)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device)
+    else:
+        _check_buf("out", out, (B, H, Nq, d), (torch.bfloat16,), q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        _check_buf("lse", lse, (B, H, Nq), (torch.float32,), q.device)
+    rc = load().attn_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d,
+                                    int(causal), float(scale), int(splits), _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_decode_noalloc")
+    return out, lse
+
+
 def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  block_table: torch.Tensor, seq_lens: torch.Tensor, *, causal: bool = False,
                  scale: float | None = None, splits: int | None = None,
@@ -339,5 +379,5 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out, lse
 
 
-__all__ = ["fwd", "quantize", "merge", "decode", "decode_paged", "default_splits", "load", "strerror", "version", "AttnError", "LIB_PATH",
+__all__ = ["fwd", "quantize", "merge", "decode", "decode_paged", "decode_noalloc", "default_splits", "load", "strerror", "version", "AttnError", "LIB_PATH",
            "SIGNATURES", "BLOCK_ROWS", "DTYPE_BF16", "DTYPE_FP8_E4M3", "DTYPE_FP8_PV"]

@@ -7,11 +7,14 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 using namespace mi355attn;
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 6 * 100 + 0;
 constexpr long long kMaxGrid = 2147483647LL;  // gridDim.x limit
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -151,34 +154,113 @@ extern "C" size_t attn_decode_workspace_bytes(int B, int H, int Nq, int d, int s
   return decode_workspace_bytes((long long)B * H * Nq, d, splits);
 }
 
-extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int H, int Nq, int Nk, int d, int causal, float scale,
-                           int splits, void* workspace, size_t workspace_bytes, void* stream) {
-  bool empty = false;
-  int rc = check_decode(B, H, Nq, Nk, d, splits, &empty);
-  if (rc != ATTN_OK || empty) return rc;
+namespace {
+
+// The checks of attn_decode that do not involve the workspace: sizes, null
+// pointers, flags, alignment, and outputs overlapping inputs or each other.
+// *need is the workspace the call needs; *empty is set for an empty problem.
+int check_decode_call(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int Nq, int Nk, int d, int causal, float scale, int splits,
+                      size_t* need, bool* empty) {
+  int rc = check_decode(B, H, Nq, Nk, d, splits, empty);
+  if (rc != ATTN_OK || *empty) return rc;
   if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
   if (causal != 0 && causal != 1) return ATTN_E_WINDOW;
   if (!isfinite(scale)) return ATTN_E_SCALE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return ATTN_E_ALIGN;
   const long long rows = (long long)B * H * Nq;
-  const size_t need = decode_workspace_bytes(rows, d, splits);
-  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return ATTN_E_WORKSPACE;
+  *need = decode_workspace_bytes(rows, d, splits);
   const size_t q_bytes = (size_t)rows * d * 2;
   const size_t kv_bytes = (size_t)B * H * Nk * d * 2;
   const size_t lse_bytes = (size_t)rows * sizeof(float);
   const void* ins[3] = {q, k, v};
   const size_t in_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
-  for (int i = 0; i < 3; ++i) {
-    if (overlap(o, q_bytes, ins[i], in_bytes[i]) || overlap(lse, lse_bytes, ins[i], in_bytes[i]) ||
-        overlap(workspace, need, ins[i], in_bytes[i]))
+  for (int i = 0; i < 3; ++i)
+    if (overlap(o, q_bytes, ins[i], in_bytes[i]) || overlap(lse, lse_bytes, ins[i], in_bytes[i]))
       return ATTN_E_ALIAS;
-  }
-  if (overlap(o, q_bytes, lse, lse_bytes) || overlap(o, q_bytes, workspace, need) ||
+  if (overlap(o, q_bytes, lse, lse_bytes)) return ATTN_E_ALIAS;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                           int splits, void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  size_t need = 0;
+  int rc = check_decode_call(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, splits, &need, &empty);
+  if (rc != ATTN_OK || empty) return rc;
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return ATTN_E_WORKSPACE;
+  const long long rows = (long long)B * H * Nq;
+  const size_t q_bytes = (size_t)rows * d * 2;
+  const size_t kv_bytes = (size_t)B * H * Nk * d * 2;
+  const size_t lse_bytes = (size_t)rows * sizeof(float);
+  if (overlap(workspace, need, q, q_bytes) || overlap(workspace, need, k, kv_bytes) ||
+      overlap(workspace, need, v, kv_bytes) || overlap(o, q_bytes, workspace, need) ||
       overlap(lse, lse_bytes, workspace, need))
     return ATTN_E_ALIAS;
   DecodeArgs a{q, k, v, o, lse, workspace, B * H, Nq, Nk, d, causal, splits, scale};
+  const hipError_t e = launch_attn_decode(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+// ---- attn_decode_noalloc: attn_decode with the library's own scratch.
+//
+// The fp32 partials and log-sum-exps live in this array instead of a
+// caller's workspace. Each device the library runs on holds its own copy from
+// the moment the code object is loaded until the process ends. In host code
+// the name `scratch` is only a host-side stand-in; the kernels get the
+// address of the copy on the launch stream's device, looked up once per
+// device with that device current and kept in g_scratch. The decode kernel writes every partial slot
+// of a call (an empty key chunk writes o = 0, lse = -inf) before the merge
+// reads it, so nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the copy of `scratch` on the device `stream` belongs to
+// (the current device for the NULL stream), looked up once per device with
+// that device current; nullptr if the device cannot be determined.
+void* scratch_for_stream(hipStream_t stream) {
+  int dev = -1;
+  if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+    return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" int attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                                   int splits, void* stream) {
+  bool empty = false;
+  size_t need = 0;
+  int rc = check_decode_call(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, splits, &need, &empty);
+  if (rc != ATTN_OK || empty) return rc;
+  if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_E_SCRATCH;
+  void* ws = scratch_for_stream((hipStream_t)stream);
+  if (!ws) return ATTN_E_LAUNCH;
+  DecodeArgs a{q, k, v, o, lse, ws, B * H, Nq, Nk, d, causal, splits, scale};
   const hipError_t e = launch_attn_decode(a, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
@@ -242,6 +324,7 @@ extern "C" const char* attn_strerror(int code) {
     case ATTN_E_LAUNCH: return "kernel launch failed (no usable GPU or invalid stream)";
     case ATTN_E_SCALE: return "scale must be finite";
     case ATTN_E_WORKSPACE: return "decode workspace is NULL, misaligned or smaller than attn_decode_workspace_bytes";
+    case ATTN_E_SCRATCH: return "attn_decode_noalloc needs more scratch than its static buffer holds (ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }
