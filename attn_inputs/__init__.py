@@ -11,7 +11,9 @@ Recipe (the same for every workload):
   * fp32 standard normal values of shape [N, d] per head;
   * for the outlier workload, 4 of the d channels (one seeded draw, shared by
     Q, K and V and by every head) are multiplied by 10 before rounding;
-  * round-to-nearest-even to bf16 (torch's fp32 -> bf16 cast).
+  * round-to-nearest-even to bf16 (torch's fp32 -> bf16 cast);
+  * the random signs of the incoherent-processing rotation of Q and K: one
+    seeded draw of d values, -1 or +1 (rotation_signs).
 
 The workloads follow the "sequence length 8192, head dim 128, batch 16"
 measurement of page "Warp Group Cluster 优化" (section 性能与适用场景), the
@@ -68,6 +70,13 @@ def outlier_channels(seed: int, d: int, count: int = 4) -> np.ndarray:
     """The channel indices scaled by 10 (one draw per seed, shared by Q, K, V)."""
     rng = np.random.default_rng([seed, 99])
     return np.sort(rng.permutation(d)[:count])
+
+
+def rotation_signs(seed: int, d: int) -> np.ndarray:
+    """d random signs (int8, -1 or +1) for the incoherent-processing rotation
+    of Q and K: one seeded draw, shared by Q and K and by every head."""
+    rng = np.random.default_rng([seed, 77])
+    return np.where(rng.random(d) < 0.5, -1, 1).astype(np.int8)
 
 
 def head_fp32(seed: int, tensor: str, b: int, h: int, N: int, d: int,

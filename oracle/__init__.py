@@ -12,6 +12,9 @@ Modules
              recurrence, both fp64
   fp8        the OCP E4M3FN number format and the per-block / per-tensor
              quantiser, from the format definition
+  rotation   incoherent processing: the random-sign Hadamard rotation of Q
+             and K (its definition in fp64, and the fp32 butterfly whose
+             values decide the rotated quantiser's codes)
   decode     attention of a few queries against a longer key/value sequence
              (the last positions, bottom-right causal alignment), fp64
   merge      the merge of partial results over disjoint key sets (their
@@ -40,6 +43,7 @@ from .fp8 import (E4M3_MAX, e4m3_decode_table, e4m3_decode, e4m3_encode,
 from .decode import attention_decode
 from .paged import attention_decode_paged, gather_pages
 from .merge import lse_merge
+from .rotation import hadamard_matrix, rotate, rotate_fp32, fwht_fp32
 from .metrics import max_abs, l1_rel, rmse_rel
 
 __all__ = [
@@ -47,5 +51,5 @@ __all__ = [
     "attention_rows", "E4M3_MAX", "e4m3_decode_table", "e4m3_decode",
     "e4m3_encode", "quantize", "dequantize", "QUANT_BLOCK_ROWS", "max_abs",
     "l1_rel", "rmse_rel", "lse_merge", "attention_decode", "attention_decode_paged",
-    "gather_pages",
+    "gather_pages", "hadamard_matrix", "rotate", "rotate_fp32", "fwht_fp32",
 ]

@@ -104,12 +104,19 @@ def _to_f32(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float32)
 
 
-def quantize(x, per_tensor: bool = False, block_rows: int = QUANT_BLOCK_ROWS):
+def quantize(x, per_tensor: bool = False, block_rows: int = QUANT_BLOCK_ROWS,
+             rotation_signs=None):
     """Quantise x [B, H, N, d] to E4M3 codes with per-block descales.
 
+    rotation_signs: d signs; when given, every row is first rotated as the
+    incoherent-processing quantiser does (oracle.rotation.rotate_fp32), and
+    the codes and descales are those of the rotated tensor.
     Returns (codes uint8 [B, H, N, d], descale float32 [B, H, ceil(N/128)]).
     """
     x = _to_f32(x)
+    if rotation_signs is not None:
+        from .rotation import rotate_fp32
+        x = rotate_fp32(x, rotation_signs)
     B, H, N, d = x.shape
     nb = -(-N // block_rows)
     codes = np.zeros(x.shape, dtype=np.uint8)
