@@ -252,9 +252,10 @@ def bench_fp8(tafa, dev, steps, warmup, stream):
     """The x10-outlier workload: all-E4M3 (per block and per tensor) and the fp8
     PV mode, at B8 (accuracy and speed) and B16 (speed, the headline shape)."""
     import torch
-    from attn_inputs import BY_NAME, workload_qkv
+    from attn_inputs import BY_NAME, workload_qkv, rotation_signs
     wf = BY_NAME[FP8_WORKLOAD]
     res = {"workload": wf.name, "dtype": "fp8_e4m3", "accuracy_bar_rmse_rel": 3e-2}
+    signs = torch.from_numpy(rotation_signs(wf.seed, wf.d)).to(dev)
     for B in (wf.B, 16):
         print(f"[bench] fp8: generating {wf.name} at B={B}", file=sys.stderr, flush=True)
         q, k, v = workload_qkv(wf, device=dev, B=B)
@@ -279,13 +280,24 @@ def bench_fp8(tafa, dev, steps, warmup, stream):
             quant()
             attn8()
 
+        def quant_rot():
+            # incoherent processing: Q and K rotated with the same signs, V plain
+            for name, t in (("q", q), ("k", k)):
+                tafa.quantize(t, out=bufs[name][0], descale=bufs[name][1], rotation_signs=signs)
+            tafa.quantize(v, out=bufs["v"][0], descale=bufs["v"][1])
+
         print(f"[bench] fp8: timing at B={B}", file=sys.stderr, flush=True)
         quant()
         _, ev_a = time_launches(attn8, steps, warmup, stream)
         _, ev_q = time_launches(quant, steps, warmup, stream)
         wall8, _ = time_launches(step8, steps, warmup, stream)
         _, ev_pv = time_launches(attn_pv, max(1, steps // 2), warmup, stream)
+        _, ev_qr = time_launches(quant_rot, steps, warmup, stream)
+        quant_rot()
+        _, ev_ar = time_launches(attn8, max(1, steps // 2), warmup, stream)
+        quant()
         a_ms, q_ms, pv_ms = mean_ms(ev_a), mean_ms(ev_q), mean_ms(ev_pv)
+        qr_ms, ar_ms = mean_ms(ev_qr), mean_ms(ev_ar)
         qbytes = 3 * q.numel() * (2 + 1) + 3 * bufs["q"][1].numel() * 4
         a_tf, pv_tf = flop / (a_ms * 1e-3) / 1e12, flop / (pv_ms * 1e-3) / 1e12
         entry = {
@@ -298,6 +310,15 @@ def bench_fp8(tafa, dev, steps, warmup, stream):
                 "quantize_frac_of_hbm_peak": round(qbytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 "end_to_end_ms_per_step": round(wall8, 4),
                 "end_to_end_tflops": round(flop / (wall8 * 1e-3) / 1e12, 2)},
+            "rotated_qk": {
+                "what": "incoherent processing: Q and K quantised after a random-sign Hadamard "
+                        "rotation (attn_fp8_quantize_rotated), V plainly; the all-E4M3 kernel",
+                "avg_launch_ms": round(ar_ms, 4),
+                "tflops": round(flop / (ar_ms * 1e-3) / 1e12, 2),
+                "frac_of_dense_fp8_peak": round(flop / (ar_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                "quantize_qkv_ms": round(qr_ms, 4),
+                "quantize_gbs": round(qbytes / (qr_ms * 1e-3) / 1e9, 1),
+                "end_to_end_tflops": round(flop / ((ar_ms + qr_ms) * 1e-3) / 1e12, 2)},
             "pv_mode": {
                 "what": "bf16 Q, K (scores on bf16 MFMAs); E4M3 V and P (PV on fp8 MFMAs)",
                 "avg_launch_ms": round(pv_ms, 4), "tflops": round(pv_tf, 2),
@@ -320,6 +341,9 @@ def bench_fp8(tafa, dev, steps, warmup, stream):
             quant(per_tensor=True)
             attn8()
             outs["per_tensor_naive"] = take(o)
+            quant_rot()
+            attn8()
+            outs["rotated_qk"] = take(o)
             quant()
             res["_samples"] = (wf, outs, heads, rows)
         res[f"B{B}"] = entry

@@ -309,6 +309,36 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
 int attn_fp8_quantize(const void* x_bf16, void* x_fp8, float* descale,
                       int B, int H, int N, int d, int per_tensor, void* stream);
 
+/*
+ * attn_fp8_quantize_rotated - attn_fp8_quantize of the rotated tensor: the
+ * incoherent processing that [JJ] (introduction, contribution 3, and section
+ * 3's summary) pairs with FP8 block quantisation. Every row x (d values) is
+ * first replaced by
+ *   x' = (x * s) H / sqrt(d)
+ * with H the d x d Sylvester Hadamard matrix (H_1 = [1], H_2n = [[H_n, H_n],
+ * [H_n, -H_n]]) and s the caller's signs; then x' is quantised exactly as
+ * attn_fp8_quantize quantises x (per 128-row block or per tensor). The matrix
+ * diag(s) H / sqrt(d) is orthogonal, so quantising Q and K with the SAME signs
+ * and passing the codes and descales to attn_fwd (dtype 1) computes the same
+ * attention: (Q M)(K M)^T = Q K^T. Channels that are large in both Q and K
+ * are spread over all d channels, which lowers the E4M3 score error. V is
+ * quantised with attn_fp8_quantize, unrotated.
+ * The rotation is computed in fp32 in this order (its values decide the
+ * codes): sign flips; the fast Walsh-Hadamard butterfly with stages
+ * h = 1, 2, 4, ..., d/2, where for every j with bit h clear x[j] becomes
+ * x[j] + x[j+h] and x[j+h] becomes x[j] - x[j+h] (one fp32 rounding each);
+ * one fp32 multiply by fp32(1/sqrt(d)).
+ *
+ *   signs     int8 [d] device memory, 8-byte aligned, read only: entry c < 0
+ *             means s_c = -1, any other value s_c = +1. Draw them at random
+ *             once and use them for both Q and K.
+ *   other arguments as in attn_fp8_quantize (d = 64 or 128).
+ * Returns ATTN_OK or an ATTN_E_* code (ATTN_E_NULL for NULL signs).
+ */
+int attn_fp8_quantize_rotated(const void* x_bf16, void* x_fp8, float* descale,
+                              const signed char* signs, int B, int H, int N, int d,
+                              int per_tensor, void* stream);
+
 /* Static, human-readable text for a return code (never NULL). */
 const char* attn_strerror(int code);
 

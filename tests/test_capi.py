@@ -40,14 +40,14 @@ def test_library_exports_every_declared_function(lib):
     names = header_functions()
     assert set(names) == {"attn_fwd", "attn_fp8_quantize", "attn_lse_merge", "attn_decode",
                           "attn_decode_workspace_bytes", "attn_decode_paged", "attn_decode_noalloc",
-                          "attn_strerror", "attn_version"}
+                          "attn_fp8_quantize_rotated", "attn_strerror", "attn_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(tafa.SIGNATURES)
 
 
 def test_version_and_strerror(lib):
-    assert tafa.version() == 10600
+    assert tafa.version() == 10700
     codes = header_codes()
     assert codes["ATTN_OK"] == 0
     texts = {tafa.strerror(c) for c in codes.values()}
@@ -298,3 +298,22 @@ def test_decode_noalloc_scratch_limit(lib):
     assert need <= limit < lib.attn_decode_workspace_bytes(4, 8, 32, 128, 32)
     assert call_noalloc(lib, B=4, H=8, Nq=32, Nk=4096, splits=32) == E["ATTN_E_SCRATCH"]
     assert call_noalloc(lib, Nq=0, q=None) == E["ATTN_OK"]
+
+
+def call_rot(lib, x=A, x8=A + GAP, ds=A + 2 * GAP, signs=A + 3 * GAP, B=2, H=3, N=300, d=128, pt=0):
+    return lib.attn_fp8_quantize_rotated(x, x8, ds, signs, B, H, N, d, pt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(signs=None), "ATTN_E_NULL"), (dict(x=None), "ATTN_E_NULL"),
+    (dict(signs=A + 3 * GAP + 4), "ATTN_E_ALIGN"), (dict(x8=A + GAP + 4), "ATTN_E_ALIGN"),
+    (dict(d=256), "ATTN_E_HEADDIM"), (dict(d=96), "ATTN_E_HEADDIM"), (dict(N=-1), "ATTN_E_SHAPE"),
+    (dict(pt=2), "ATTN_E_DTYPE"),
+    (dict(signs=A + GAP + 64), "ATTN_E_ALIAS"), (dict(signs=A + 2 * GAP), "ATTN_E_ALIAS"),
+])
+def test_quantize_rotated_rejects(lib, kw, code):
+    assert call_rot(lib, **kw) == E[code]
+
+
+def test_quantize_rotated_empty_problem_is_ok(lib):
+    assert call_rot(lib, N=0, x=None, signs=None) == E["ATTN_OK"]

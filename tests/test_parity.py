@@ -55,7 +55,7 @@ import numpy as np
 import pytest
 import torch
 
-from attn_inputs import make_qkv, workload_qkv, workload_head, BY_NAME, WORKLOADS
+from attn_inputs import make_qkv, workload_qkv, workload_head, rotation_signs, BY_NAME, WORKLOADS
 from oracle import (attention_two_pass, attention_rows, quantize as o_quantize, dequantize,
                     max_abs, l1_rel, rmse_rel)
 
@@ -303,6 +303,40 @@ def test_fp8_tiny_v_blocks(lib):
         check_fp8_vs_dequantised(o, lse, codes, scale, causal, -1, f"tiny V causal={causal}", False)
 
 
+@pytest.mark.parametrize("B,H,N,d", QSHAPES)
+@pytest.mark.parametrize("per_tensor", [False, True])
+@pytest.mark.parametrize("outliers", [False, True])
+def test_quantize_rotated_bit_exact(lib, B, H, N, d, per_tensor, outliers):
+    """attn_fp8_quantize_rotated against the oracle's rotated quantiser: the
+    fp32 butterfly in the same stage order gives the same values, so codes
+    and descales agree bit for bit."""
+    x, _, _ = make_qkv(B, H, N, d, seed=140 + N, outliers=outliers)
+    x = x * 3
+    s = rotation_signs(150 + d, d)
+    x8, ds = lib.quantize(x.cuda(), per_tensor=per_tensor, rotation_signs=torch.from_numpy(s).cuda())
+    torch.cuda.synchronize()
+    rc, rds = o_quantize(x, per_tensor=per_tensor, rotation_signs=s)
+    assert np.array_equal(x8.cpu().numpy(), rc)
+    assert np.array_equal(ds.cpu().numpy(), rds)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_quantize_rotated_tiny_and_wide_range_rows(lib, d):
+    # rows whose values span many binades (the butterfly's roundings matter)
+    # and blocks under the tiny-amax rule, bit-exact
+    g = torch.Generator().manual_seed(160 + d)
+    x = torch.randn(1, 1, 768, d, generator=g, dtype=torch.float64)
+    x = x * torch.exp(torch.empty(1, 1, 768, d, dtype=torch.float64).uniform_(-12, 12, generator=g))
+    x[0, 0, 256:384] *= 1e-37
+    x[0, 0, 384:512] = 0.0
+    x = x.to(torch.bfloat16)
+    s = rotation_signs(170 + d, d)
+    x8, ds = lib.quantize(x.cuda(), rotation_signs=torch.from_numpy(s).cuda())
+    torch.cuda.synchronize()
+    rc, rds = o_quantize(x, rotation_signs=s)
+    assert np.array_equal(x8.cpu().numpy(), rc) and np.array_equal(ds.cpu().numpy(), rds)
+
+
 def fp8_run(lib, q, k, v, per_tensor, causal=False, window=-1, scale=None):
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     (q8, dq), (k8, dk), (v8, dv) = [lib.quantize(t, per_tensor=per_tensor) for t in (qd, kd, vd)]
@@ -391,6 +425,24 @@ def test_fp8_vs_dequantised_oracle(lib, B, H, N, d, causal, window, outliers):
     o, lse, codes = fp8_run(lib, q, k, v, False, causal, window, scale)
     check_fp8_vs_dequantised(o, lse, codes, scale, causal, window,
                              f"{(B, H, N, d, causal, window, outliers)}", outliers)
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 2, 127, 128), (2, 2, 300, 128), (1, 1, 1000, 64), (1, 1, 333, 64)])
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 100)])
+def test_fp8_rotated_qk_vs_dequantised_oracle(lib, B, H, N, d, causal, window):
+    """Q and K quantised after the random-sign Hadamard rotation, V plainly;
+    the kernel against the oracle on the dequantised (rotated) inputs, within
+    the same bound as every all-E4M3 case."""
+    q, k, v = make_qkv(B, H, N, d, seed=180 + N, outliers=True)
+    scale = 1 / math.sqrt(d)
+    sg = torch.from_numpy(rotation_signs(190 + d, d)).cuda()
+    (q8, dq), (k8, dk) = [lib.quantize(t.cuda(), rotation_signs=sg) for t in (q, k)]
+    v8, dv = lib.quantize(v.cuda())
+    o, lse = lib.fwd(q8, k8, v8, descales=(dq, dk, dv), causal=causal, window=window, scale=scale)
+    torch.cuda.synchronize()
+    codes = [t.cpu().numpy() for t in (q8, dq, k8, dk, v8, dv)]
+    check_fp8_vs_dequantised(o.cpu(), lse.cpu(), codes, scale, causal, window,
+                             f"rotated {(B, H, N, d, causal, window)}", True)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -541,22 +593,26 @@ def test_fp8_outlier_workload_full_size(lib):
     of the oracle on its own dequantised inputs. Sampled heads and rows."""
     w = BY_NAME["noncausal_b8h16n8192d128_fp8_outliers"]
     q, k, v = workload_qkv(w, device="cuda")
+    sg = torch.from_numpy(rotation_signs(w.seed, w.d)).cuda()
     res = {}
-    for per_tensor in (False, True):
-        (q8, dq), (k8, dk), (v8, dv) = [lib.quantize(t, per_tensor=per_tensor) for t in (q, k, v)]
+    for mode in (False, True, "rotated"):
+        per_tensor = mode is True
+        rot = sg if mode == "rotated" else None
+        (q8, dq), (k8, dk) = [lib.quantize(t, per_tensor=per_tensor, rotation_signs=rot) for t in (q, k)]
+        v8, dv = lib.quantize(v, per_tensor=per_tensor)
         o, lse = lib.fwd(q8, k8, v8, descales=(dq, dk, dv), scale=w.scale)
         torch.cuda.synchronize()
-        res[per_tensor] = (o.cpu(), lse.cpu(), [t.cpu().numpy() for t in (q8, dq, k8, dk, v8, dv)])
+        res[mode] = (o.cpu(), lse.cpu(), [t.cpu().numpy() for t in (q8, dq, k8, dk, v8, dv)])
         del q8, k8, v8, o, lse
     del q, k, v
-    errs = {False: [], True: []}
+    errs = {False: [], True: [], "rotated": []}
     for (b, h) in SPREAD_8x16:
         qh, kh, vh = workload_head(w, b, h)
         rows = sampled_rows(w.N, 256, 300 + b * 31 + h)
         ref_o, _ = attention_rows(qh, kh, vh, w.scale, False, -1, rows)
-        for per_tensor in (False, True):
-            o, lse, codes = res[per_tensor]
-            errs[per_tensor].append((o[b, h, rows].double() - ref_o).pow(2).mean() / ref_o.pow(2).mean())
+        for mode in errs:
+            o, lse, codes = res[mode]
+            errs[mode].append((o[b, h, rows].double() - ref_o).pow(2).mean() / ref_o.pow(2).mean())
         o, lse, codes = res[False]
         q8, dq, k8, dk, v8, dv = codes
         sl = lambda c, d_: torch.from_numpy(dequantize(c[b:b + 1, h:h + 1], d_[b:b + 1, h:h + 1])[0, 0])
@@ -569,8 +625,11 @@ def test_fp8_outlier_workload_full_size(lib):
         assert r <= FP8_RMSE_REL
     rm_block = math.sqrt(float(sum(errs[False]) / len(errs[False])))
     rm_tensor = math.sqrt(float(sum(errs[True]) / len(errs[True])))
-    print(f"fp8 outlier workload RMSE/RMS: per-block {rm_block:.4f} per-tensor {rm_tensor:.4f}")
+    rm_rot = math.sqrt(float(sum(errs["rotated"]) / len(errs["rotated"])))
+    print(f"fp8 outlier workload RMSE/RMS: per-block {rm_block:.4f} per-tensor {rm_tensor:.4f} "
+          f"rotated Q, K per-block {rm_rot:.4f} ({rm_tensor / rm_rot:.2f}x below per-tensor)")
     assert rm_block < rm_tensor
+    assert rm_rot < rm_block
 
 
 # ---- fp8 PV mode: q, k bf16 (scores on bf16 MFMAs), v and P in E4M3

@@ -36,6 +36,7 @@ _f = ctypes.c_float
 SIGNATURES = {
     "attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp]),
     "attn_fp8_quantize": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "attn_fp8_quantize_rotated": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "attn_lse_merge": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
@@ -172,12 +173,19 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
 
 
 def quantize(x: torch.Tensor, per_tensor: bool = False, out: torch.Tensor | None = None,
-             descale: torch.Tensor | None = None, stream=None):
-    """bf16 [B,H,N,d] -> (E4M3 codes uint8 [B,H,N,d], fp32 descale [B,H,ceil(N/128)])."""
+             descale: torch.Tensor | None = None, stream=None,
+             rotation_signs: torch.Tensor | None = None):
+    """bf16 [B,H,N,d] -> (E4M3 codes uint8 [B,H,N,d], fp32 descale [B,H,ceil(N/128)]).
+
+    rotation_signs: int8 [d] on x's device; when given, the rows are rotated
+    first (attn_fp8_quantize_rotated, incoherent processing). Quantise Q and K
+    with the same signs; V without."""
     _check_4d("x", x)
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bf16")
     B, H, N, d = x.shape
+    if rotation_signs is not None:
+        _check_buf("rotation_signs", rotation_signs, (d,), (torch.int8,), x.device)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
     else:
@@ -186,10 +194,16 @@ def quantize(x: torch.Tensor, per_tensor: bool = False, out: torch.Tensor | None
         descale = torch.empty((B, H, -(-N // BLOCK_ROWS)), dtype=torch.float32, device=x.device)
     else:
         _check_buf("descale", descale, (B, H, -(-N // BLOCK_ROWS)), (torch.float32,), x.device)
-    rc = load().attn_fp8_quantize(_ptr(x), _ptr(out), _ptr(descale), B, H, N, d,
-                                  int(per_tensor), _stream(stream))
+    if rotation_signs is None:
+        rc = load().attn_fp8_quantize(_ptr(x), _ptr(out), _ptr(descale), B, H, N, d,
+                                      int(per_tensor), _stream(stream))
+        what = "attn_fp8_quantize"
+    else:
+        rc = load().attn_fp8_quantize_rotated(_ptr(x), _ptr(out), _ptr(descale), _ptr(rotation_signs),
+                                              B, H, N, d, int(per_tensor), _stream(stream))
+        what = "attn_fp8_quantize_rotated"
     if rc != 0:
-        raise AttnError(rc, "attn_fp8_quantize")
+        raise AttnError(rc, what)
     return out, descale
 
 

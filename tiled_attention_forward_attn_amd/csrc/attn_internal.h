@@ -50,7 +50,9 @@ hipError_t launch_attn_fwd_fp8(const FwdArgs& a, bool qk_bf16, hipStream_t strea
 // rows = B * H * N; d in {64, 128, 256}.
 hipError_t launch_lse_merge(const float* o_part, const float* lse_part, int R, long long rows, int d,
                             void* o, float* lse, hipStream_t stream);
-hipError_t launch_fp8_quantize(const void* x, void* x8, float* descale, int BH, int N, int d,
-                               int per_tensor, hipStream_t stream);
+// signs: nullptr for the plain quantiser; else d signs of the rotation
+// (incoherent processing) applied to every row first.
+hipError_t launch_fp8_quantize(const void* x, void* x8, float* descale, const int8_t* signs, int BH,
+                               int N, int d, int per_tensor, hipStream_t stream);
 
 }  // namespace mi355attn

@@ -14,7 +14,7 @@ using namespace mi355attn;
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 6 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 7 * 100 + 0;
 constexpr long long kMaxGrid = 2147483647LL;  // gridDim.x limit
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -89,22 +89,42 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
-extern "C" int attn_fp8_quantize(const void* x_bf16, void* x_fp8, float* descale, int B, int H,
-                                 int N, int d, int per_tensor, void* stream) {
+namespace {
+
+// attn_fp8_quantize and attn_fp8_quantize_rotated (signs != nullptr).
+int quantize_call(const void* x_bf16, void* x_fp8, float* descale, const signed char* signs,
+                  bool rotated, int B, int H, int N, int d, int per_tensor, void* stream) {
   bool empty = false;
   int rc = check_shape(B, H, N, d, false, &empty);
   if (rc != ATTN_OK || empty) return rc;
-  if (!x_bf16 || !x_fp8 || !descale) return ATTN_E_NULL;
+  if (!x_bf16 || !x_fp8 || !descale || (rotated && !signs)) return ATTN_E_NULL;
   if (per_tensor != 0 && per_tensor != 1) return ATTN_E_DTYPE;
-  if (!aligned(x_bf16, 16) || !aligned(x_fp8, 8) || !aligned(descale, 4)) return ATTN_E_ALIGN;
+  if (!aligned(x_bf16, 16) || !aligned(x_fp8, 8) || !aligned(descale, 4) ||
+      (rotated && !aligned(signs, 8)))
+    return ATTN_E_ALIGN;
   const size_t elems = (size_t)B * H * N * d;
   const size_t ds_bytes = (size_t)B * H * ((N + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS) * sizeof(float);
   if (overlap(x_fp8, elems, x_bf16, elems * 2) || overlap(descale, ds_bytes, x_bf16, elems * 2) ||
       overlap(descale, ds_bytes, x_fp8, elems))
     return ATTN_E_ALIAS;
-  const hipError_t e = launch_fp8_quantize(x_bf16, x_fp8, descale, B * H, N, d, per_tensor,
-                                           (hipStream_t)stream);
+  if (rotated && (overlap(x_fp8, elems, signs, d) || overlap(descale, ds_bytes, signs, d)))
+    return ATTN_E_ALIAS;
+  const hipError_t e = launch_fp8_quantize(x_bf16, x_fp8, descale, (const int8_t*)signs, B * H, N, d,
+                                           per_tensor, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_fp8_quantize(const void* x_bf16, void* x_fp8, float* descale, int B, int H,
+                                 int N, int d, int per_tensor, void* stream) {
+  return quantize_call(x_bf16, x_fp8, descale, nullptr, false, B, H, N, d, per_tensor, stream);
+}
+
+extern "C" int attn_fp8_quantize_rotated(const void* x_bf16, void* x_fp8, float* descale,
+                                         const signed char* signs, int B, int H, int N, int d,
+                                         int per_tensor, void* stream) {
+  return quantize_call(x_bf16, x_fp8, descale, signs, true, B, H, N, d, per_tensor, stream);
 }
 
 extern "C" int attn_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,

@@ -27,6 +27,19 @@
 //      its own slot and overwriting that slot with the descale,
 // so no workspace, atomic or memset is needed and no slot is read after
 // another block has overwritten it.
+//
+// Rotated mode (incoherent processing, [JJ] introduction and section 3: the
+// page pairs FP8 block quantisation with it): every row x is replaced, before
+// the block's amax and conversion, by its rotation x diag(s) H / sqrt(d) (H
+// the Sylvester Hadamard matrix, s the caller's random signs). Applied with
+// the same signs to Q and K it leaves Q K^T unchanged while spreading
+// channels that are large in both over all d channels. Computed in fp32 in a
+// fixed order, since these values decide the codes: sign flips (exact); the
+// fast Walsh-Hadamard butterfly with stages h = 1, 2, ..., d/2, each output
+// one rounded fp32 sum (j with bit h clear: x[j] + x[j+h]) or difference
+// (x[j] - x[j+h]); one multiply by fp32(1/sqrt(d)). A row's d / 8 chunks of
+// 8 values sit in d / 8 consecutive lanes, so stages 1, 2, 4 are in-lane and
+// stage 8 m (m = 1, 2, ...) pairs lane l with lane l ^ m.
 #include "attn_internal.h"
 
 #include <math.h>
@@ -68,30 +81,96 @@ __device__ __forceinline__ int cvt4(float a, float b, float c, float d) {
 
 __device__ __forceinline__ float sat(float y) { return fminf(fmaxf(y, -kE4M3Max), kE4M3Max); }
 
-template <int D, int MODE>
+// fp32(1 / sqrt(d)): the rotation's normalisation.
+template <int D>
+constexpr float inv_sqrt_d() { return D == 128 ? 0.08838834764831845f : 0.125f; }
+
+// The 8 values of one chunk as fp32 (bf16 bits, exact).
+__device__ __forceinline__ void unpack8(i32x4 w, float (&v)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = bf16_lo(w[e]);
+    v[2 * e + 1] = bf16_hi(w[e]);
+  }
+}
+
+// Rotation of the row this lane holds chunk `col` of (see the header): sign
+// flips from the lane's sign mask bits, in-lane butterfly stages 1, 2, 4,
+// cross-lane stages 8 .. D/2 (lane ^ m), then the normalisation.
+template <int D>
+__device__ __forceinline__ void rotate_chunk(float (&v)[8], int col, uint32_t sign_bits) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((sign_bits >> e) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (!(e & h)) {
+        const float a = v[e], b = v[e + h];
+        v[e] = a + b;
+        v[e + h] = a - b;
+      }
+#pragma unroll
+  for (int m = 1; m < D / 8; m <<= 1) {
+    const bool upper = (col & m) != 0;   // holds x[j + h]; the partner holds x[j]
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __shfl_xor(v[e], m);
+      v[e] = upper ? p - v[e] : v[e] + p;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = v[e] * inv_sqrt_d<D>();
+}
+
+// ROT: rotate every row first (see the header); `signs` holds the d signs
+// (a byte < 0 means -1). Without ROT, signs is unused.
+template <int D, int MODE, bool ROT>
 __global__ __launch_bounds__(kThreads)
 void fp8_quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
-                      float* __restrict__ descale, int N, int nb) {
+                      float* __restrict__ descale, const int8_t* __restrict__ signs, int N, int nb) {
   constexpr int DCH = D / 8;                       // 16-byte chunks per row
   constexpr int LOADS = kRows * DCH / kThreads;    // 8 at d = 128, 4 at d = 64
+  static_assert(kThreads % DCH == 0, "a lane keeps its column in every round");
   __shared__ float red[kThreads / 64];
 
   const int blk = blockIdx.x;                      // (bh, rb) flattened
   const int bh = blk / nb, rb = blk % nb;
   const size_t head = (size_t)bh * N * D;
   const int tid = threadIdx.x;
+  const int col = tid % DCH;                       // this lane's chunk of every row it holds
 
-  i32x4 x[LOADS];
+  uint32_t sign_bits = 0;
+  if constexpr (ROT) {
+    const i32x2 sw = *(const i32x2*)(signs + col * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      sign_bits |= (uint32_t)((((e < 4 ? sw[0] : sw[1]) >> (8 * (e & 3) + 7)) & 1)) << e;
+  }
+
+  // the block's values: packed bf16 as loaded, or (ROT) the rotated fp32
+  i32x4 x[ROT ? 1 : LOADS];
+  float v[ROT ? LOADS : 1][8];
   float amax = 0.f;
 #pragma unroll
   for (int u = 0; u < LOADS; ++u) {
     const int chunk = tid + u * kThreads;
-    const int row = rb * kRows + chunk / DCH, col = chunk % DCH;
-    x[u] = i32x4{0, 0, 0, 0};
-    if (row < N) x[u] = __builtin_nontemporal_load((const i32x4*)(X + head + (size_t)row * D + col * 8));
+    const int row = rb * kRows + chunk / DCH;
+    i32x4 w = {0, 0, 0, 0};
+    if (row < N) w = __builtin_nontemporal_load((const i32x4*)(X + head + (size_t)row * D + col * 8));
+    float f[8];
+    unpack8(w, f);
+    if constexpr (ROT) {
+      // rows past N are zero, and so is their rotation: they add nothing to amax
+      rotate_chunk<D>(f, col, sign_bits);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(x[u][e])), fabsf(bf16_hi(x[u][e]))));
+      for (int e = 0; e < 8; ++e) v[u][e] = f[e];
+    } else {
+      x[u] = w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
   }
 
   if constexpr (MODE == kConvertFromSlot) {
@@ -109,13 +188,18 @@ void fp8_quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
 #pragma unroll
   for (int u = 0; u < LOADS; ++u) {
     const int chunk = tid + u * kThreads;
-    const int row = rb * kRows + chunk / DCH, col = chunk % DCH;
+    const int row = rb * kRows + chunk / DCH;
     if (row < N) {
+      float f[8];
+      if constexpr (ROT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = v[u][e];
+      } else {
+        unpack8(x[u], f);
+      }
       i32x2 out;
-      out[0] = cvt4(sat(bf16_lo(x[u][0]) * r), sat(bf16_hi(x[u][0]) * r),
-                    sat(bf16_lo(x[u][1]) * r), sat(bf16_hi(x[u][1]) * r));
-      out[1] = cvt4(sat(bf16_lo(x[u][2]) * r), sat(bf16_hi(x[u][2]) * r),
-                    sat(bf16_lo(x[u][3]) * r), sat(bf16_hi(x[u][3]) * r));
+      out[0] = cvt4(sat(f[0] * r), sat(f[1] * r), sat(f[2] * r), sat(f[3] * r));
+      out[1] = cvt4(sat(f[4] * r), sat(f[5] * r), sat(f[6] * r), sat(f[7] * r));
       __builtin_nontemporal_store(out, (i32x2*)(X8 + head + (size_t)row * D + col * 8));
     }
   }
@@ -137,32 +221,40 @@ void fp8_amax_broadcast_kernel(float* __restrict__ slots, int n) {
   for (int i = threadIdx.x; i < n; i += 1024) slots[i] = g;
 }
 
-template <int D>
-hipError_t launch_d(const uint16_t* x, uint8_t* x8, float* ds, int BH, int N, int per_tensor,
-                    hipStream_t s) {
+template <int D, bool ROT>
+hipError_t launch_d(const uint16_t* x, uint8_t* x8, float* ds, const int8_t* signs, int BH, int N,
+                    int per_tensor, hipStream_t s) {
   const int nb = (N + kRows - 1) / kRows;
   const int G = BH * nb;  // bounded by the C ABI's shape checks
   if (!per_tensor) {
-    hipLaunchKernelGGL((fp8_quant_kernel<D, kPerBlock>), dim3(G), dim3(kThreads), 0, s, x, x8, ds, N, nb);
+    hipLaunchKernelGGL((fp8_quant_kernel<D, kPerBlock, ROT>), dim3(G), dim3(kThreads), 0, s, x, x8, ds,
+                       signs, N, nb);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((fp8_quant_kernel<D, kAmaxOnly>), dim3(G), dim3(kThreads), 0, s, x, x8, ds, N, nb);
+  hipLaunchKernelGGL((fp8_quant_kernel<D, kAmaxOnly, ROT>), dim3(G), dim3(kThreads), 0, s, x, x8, ds,
+                     signs, N, nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fp8_amax_broadcast_kernel, dim3(1), dim3(1024), 0, s, ds, G);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fp8_quant_kernel<D, kConvertFromSlot>), dim3(G), dim3(kThreads), 0, s, x, x8, ds, N, nb);
+  hipLaunchKernelGGL((fp8_quant_kernel<D, kConvertFromSlot, ROT>), dim3(G), dim3(kThreads), 0, s, x, x8,
+                     ds, signs, N, nb);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fp8_quantize(const void* x, void* x8, float* descale, int BH, int N, int d,
-                               int per_tensor, hipStream_t stream) {
-  if (d == 128)
-    return launch_d<128>((const uint16_t*)x, (uint8_t*)x8, descale, BH, N, per_tensor, stream);
-  return launch_d<64>((const uint16_t*)x, (uint8_t*)x8, descale, BH, N, per_tensor, stream);
+hipError_t launch_fp8_quantize(const void* x, void* x8, float* descale, const int8_t* signs, int BH,
+                               int N, int d, int per_tensor, hipStream_t stream) {
+  const uint16_t* xb = (const uint16_t*)x;
+  uint8_t* q = (uint8_t*)x8;
+  if (signs) {
+    if (d == 128) return launch_d<128, true>(xb, q, descale, signs, BH, N, per_tensor, stream);
+    return launch_d<64, true>(xb, q, descale, signs, BH, N, per_tensor, stream);
+  }
+  if (d == 128) return launch_d<128, false>(xb, q, descale, nullptr, BH, N, per_tensor, stream);
+  return launch_d<64, false>(xb, q, descale, nullptr, BH, N, per_tensor, stream);
 }
 
 }  // namespace mi355attn
