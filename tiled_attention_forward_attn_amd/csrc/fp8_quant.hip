@@ -74,8 +74,13 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return r;
 }
 
+// Four E4M3 codes in one word. Each v_cvt_pk_fp8_f32 writes one half of its
+// destination and keeps the other; the second conversion overwrites the half
+// the first one keeps, so the first one's "old" value is a don't-care: a's
+// own bits (a register that dies here) rather than a zero, which would cost a
+// v_mov per word.
 __device__ __forceinline__ int cvt4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
