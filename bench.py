@@ -223,7 +223,8 @@ def bench_bf16_config(tafa, w, dev, steps, warmup, stream):
         "avg_launch_ms": round(ms, 5),
         "tflops": round(tf, 2), "algorithmic_tflop": flop / 1e12,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(w.name, "bf16")},
     }
     return entry, samples
 

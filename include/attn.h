@@ -13,9 +13,11 @@
  *   [YT]  "FlashAttention V3：优化框架吞吐量的关键技术实践"
  *
  * Conventions shared by every entry point
- *   - All tensor pointers are DEVICE pointers owned by the caller. The library
- *     never allocates, frees, copies to the host or synchronises; it keeps no
- *     state between calls apart from a cache of device properties.
+ *   - All tensor pointers are DEVICE pointers owned by the caller. No call
+ *     allocates, frees, copies to the host or synchronises. The library keeps
+ *     no state between calls apart from a cache of device properties, and one
+ *     static device buffer (ATTN_NOALLOC_SCRATCH_BYTES per device, part of its
+ *     code object) that only attn_decode_noalloc uses.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL means
  *     the default stream) and the call returns before the work finishes.
  *     Device-side faults surface at the caller's next synchronisation.
