@@ -423,7 +423,7 @@ def main():
                    "causal": w.causal, "window": w.window, "scale": w.scale,
                    "algorithmic_tflop_per_step": flop / 1e12},
         "frac_of_dense_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<128, 32, 1, 8, false>",
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<128, 64, 1, 8, false>",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(kern_ms, 4)},

@@ -86,8 +86,13 @@ struct Bf16Fwd {
   f32x16 oacc[QB][DBLK];
   f32x16 sacc[QB][NKB];
   bf16x8 pbuf[2][QB][PST];
-  bf16x8 kf[NKB][KSTEPS];
-  bf16x8 vf[PST][DBLK];
+  // Fragments streamed from LDS right before their MFMAs: the 64-key tile at
+  // d = 128 holds one 32-key block of K fragments and one 16-key step of V
+  // fragments at a time (all of a tile's would not fit two waves per SIMD).
+  // Otherwise a tile's K and V fragments are all read up front.
+  static constexpr bool STREAM = D == 128 && BN == 64;
+  bf16x8 kf[STREAM ? 1 : NKB][KSTEPS];
+  bf16x8 vf[STREAM ? 1 : PST][DBLK];
   float m[QB], l[QB], alpha[QB];
   bool owe_rescale;
 
@@ -104,66 +109,85 @@ struct Bf16Fwd {
       copy_to_lds16(vres, vl[ST] + (u * NW + wave) * 1024, voff[u], (int)((uint32_t)kt * (BN * D * 2)));
   }
 
-  // A operand of S^T = K Q^T: lane holds K[32 kb + l32][16 t + 8 h .. +7].
+  // A operand of S^T = K Q^T for 32-key block kb (into fragment set i): lane
+  // holds K[32 kb + l32][16 t + 8 h .. +7].
   template <int ST>
-  __device__ __forceinline__ void read_k() {
+  __device__ __forceinline__ void read_k_block(int kb, int i) {
     const lds_char* Ks = kl[ST];
+    const int row = kb * 32 + l32;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const int row = kb * 32 + l32;
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) {
-        const int ch = 2 * t + h;
-        kf[kb][t] = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ bf16_swz_k<D>(row)) << 4));
-      }
+    for (int t = 0; t < KSTEPS; ++t) {
+      const int ch = 2 * t + h;
+      kf[i][t] = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ bf16_swz_k<D>(row)) << 4));
     }
   }
-  // A operand of O^T += V^T P^T for MFMA step s: lane (d, h) holds V at keys
-  // 16 s + 4 h + 0..3 and + 8 (the key order of the S^T accumulator).
   template <int ST>
-  __device__ __forceinline__ void read_v() {
+  __device__ __forceinline__ void read_k() {
+    if constexpr (!STREAM) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) read_k_block<ST>(kb, kb);
+    }
+  }
+  // A operand of O^T += V^T P^T for MFMA step s (into fragment set i): lane
+  // (d, h) holds V at keys 16 s + 4 h + 0..3 and + 8 (the key order of the
+  // S^T accumulator).
+  template <int ST>
+  __device__ __forceinline__ void read_v_step(int s, int i) {
     const lds_char* Vs = vl[ST];
     const int g = lane >> 4, sl = lane & 15;
+    const int r1 = 16 * s + 4 * (g >> 1) + (sl >> 2);
+    const int r2 = r1 + 8;
 #pragma unroll
-    for (int s = 0; s < PST; ++s) {
-      const int r1 = 16 * s + 4 * (g >> 1) + (sl >> 2);
-      const int r2 = r1 + 8;
+    for (int db = 0; db < DBLK; ++db) {
+      const int col = db * 32 + 16 * (g & 1) + 4 * (sl & 3);
+      const int a1 = r1 * D * 2 + (((col >> 3) ^ bf16_swz_v<D>(r1)) << 4) + ((col >> 2) & 1) * 8;
+      const int a2 = r2 * D * 2 + (((col >> 3) ^ bf16_swz_v<D>(r2)) << 4) + ((col >> 2) & 1) * 8;
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + a1));
+      const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + a2));
+      vf[i][db] = __builtin_bit_cast(bf16x8, i16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1],
+                                                   v2[2], v2[3]});
+    }
+  }
+  template <int ST>
+  __device__ __forceinline__ void read_v() {
+    if constexpr (!STREAM) {
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int col = db * 32 + 16 * (g & 1) + 4 * (sl & 3);
-        const int a1 = r1 * D * 2 + (((col >> 3) ^ bf16_swz_v<D>(r1)) << 4) + ((col >> 2) & 1) * 8;
-        const int a2 = r2 * D * 2 + (((col >> 3) ^ bf16_swz_v<D>(r2)) << 4) + ((col >> 2) & 1) * 8;
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + a1));
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + a2));
-        vf[s][db] = __builtin_bit_cast(bf16x8, i16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1],
-                                                     v2[2], v2[3]});
-      }
+      for (int s = 0; s < PST; ++s) read_v_step<ST>(s, s);
     }
   }
 
+  // S^T of the tile in K stage ST.
+  template <int ST>
   __device__ __forceinline__ void qk() {
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sacc[b][kb] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      if constexpr (STREAM) read_k_block<ST>(kb, 0);
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t)
 #pragma unroll
         for (int b = 0; b < QB; ++b)
-          sacc[b][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][t], qf[b][t], sacc[b][kb], 0, 0, 0);
+          sacc[b][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[STREAM ? 0 : kb][t], qf[b][t],
+                                                                sacc[b][kb], 0, 0, 0);
+    }
   }
 
+  // O^T += V^T P^T with P set PB and the V tile in stage PB.
   template <int PB>
   __device__ __forceinline__ void pv() {
 #pragma unroll
-    for (int s = 0; s < PST; ++s)
+    for (int s = 0; s < PST; ++s) {
+      if constexpr (STREAM) read_v_step<PB>(s, 0);
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
 #pragma unroll
         for (int b = 0; b < QB; ++b)
-          oacc[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s][db], pbuf[PB][b][s], oacc[b][db], 0, 0, 0);
+          oacc[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[STREAM ? 0 : s][db], pbuf[PB][b][s],
+                                                                oacc[b][db], 0, 0, 0);
+    }
   }
 
   // Disallowed keys of an edge tile get score -inf. sacc[b][kb][i] is the
@@ -299,7 +323,7 @@ struct Bf16Fwd {
     issue_v<PB>(j);
     read_k<PB>();
     if constexpr (!FIRST) read_v<PB ^ 1>();
-    qk();
+    qk<PB>();
     rescale();
     if constexpr (!FIRST) pv<PB ^ 1>();
     softmax<EDGE, PB, FIRST>(j);
@@ -495,7 +519,11 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 }
 
 // Configuration per head dimension: queries per wave (32 QB), keys per tile.
-constexpr int kQB128 = 1, kBN128 = 32;
+// At d = 128 the 8-wave workgroups take 64-key tiles (fragments streamed,
+// see Bf16Fwd::STREAM): half the barriers and half the per-tile softmax
+// bookkeeping per key (+2.0 .. 2.4% at B16 H16 N8192 in a same-box A/B).
+// The 4-wave ones keep 32: there 64 measured -1% causal at N 8192.
+constexpr int kQB128 = 1, kBN128 = 32, kBN128Wide = 64;
 constexpr int kQB64 = 1, kBN64 = 64;
 // d = 256: 128 accumulator floats per lane and 64-register Q, K and V
 // fragment sets need more than the 256 registers of two waves per SIMD; one
@@ -543,7 +571,7 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
                     (long long)((a.N + 255) / 256) * a.BH >= kWideGridMin;
   const bool pair = a.causal && a.window < 0 && (a.N + 127) / 128 <= kPairMaxTiles;
   if (a.d == 128) {
-    if (wide) launch_cfg<128, kBN128, kQB128, 8, false>(a, c, qsign, qkeep, stream);
+    if (wide) launch_cfg<128, kBN128Wide, kQB128, 8, false>(a, c, qsign, qkeep, stream);
     else if (pair) launch_cfg<128, kBN128, kQB128, 4, true>(a, c, qsign, qkeep, stream);
     else launch_cfg<128, kBN128, kQB128, 4, false>(a, c, qsign, qkeep, stream);
   } else if (a.d == 256) {
