@@ -109,17 +109,18 @@ struct Bf16Fwd {
       copy_to_lds16(vres, vl[ST] + (u * NW + wave) * 1024, voff[u], (int)((uint32_t)kt * (BN * D * 2)));
   }
 
-  // A operand of S^T = K Q^T for 32-key block kb (into fragment set i): lane
-  // holds K[32 kb + l32][16 t + 8 h .. +7].
+  // A operand of S^T = K Q^T for 32-key block kb, k-step t: lane holds
+  // K[32 kb + l32][16 t + 8 h .. +7].
+  template <int ST>
+  __device__ __forceinline__ bf16x8 k_frag(int kb, int t) const {
+    const int row = kb * 32 + l32;
+    const int ch = 2 * t + h;
+    return *(const lds_bf16x8*)(kl[ST] + row * D * 2 + ((ch ^ bf16_swz_k<D>(row)) << 4));
+  }
   template <int ST>
   __device__ __forceinline__ void read_k_block(int kb, int i) {
-    const lds_char* Ks = kl[ST];
-    const int row = kb * 32 + l32;
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-      const int ch = 2 * t + h;
-      kf[i][t] = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ bf16_swz_k<D>(row)) << 4));
-    }
+    for (int t = 0; t < KSTEPS; ++t) kf[i][t] = k_frag<ST>(kb, t);
   }
   template <int ST>
   __device__ __forceinline__ void read_k() {
@@ -156,6 +157,10 @@ struct Bf16Fwd {
     }
   }
 
+  // K fragments in flight ahead of the MFMAs that use them, in k-steps, in
+  // the streamed 64-key tile (one k-step = two MFMAs = 64 MFMA cycles).
+  static constexpr int kKAhead = 3;
+
   // S^T of the tile in K stage ST.
   template <int ST>
   __device__ __forceinline__ void qk() {
@@ -163,6 +168,32 @@ struct Bf16Fwd {
     for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sacc[b][kb] = f32x16{};
+    if constexpr (STREAM && QB == 1 && NKB == 2) {
+      // The two 32-key blocks' accumulator chains advance together, k-step
+      // by k-step, and each step's two K fragments are read kKAhead steps
+      // before their MFMAs. Left to itself the compiler streams one block's
+      // fragments into a single register set, so each of its MFMAs waits a
+      // whole LDS round trip; this order hides the round trips (about 2% at
+      // B16 H16 N8192 in a same-box A/B, bit-identical outputs).
+      bf16x8 f[KSTEPS][NKB];
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) f[t][kb] = k_frag<ST>(kb, t);
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          sacc[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[t][kb], qf[0][t], sacc[0][kb], 0, 0, 0);
+      // scheduling groups: 0x100 = LDS reads, 0x008 = MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKAhead, 0);
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (t + kKAhead < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       if constexpr (STREAM) read_k_block<ST>(kb, 0);
