@@ -124,7 +124,7 @@ struct Bf16Fwd {
   }
   template <int ST>
   __device__ __forceinline__ void read_k() {
-    if constexpr (!STREAM) {
+    if constexpr (!STREAM && !SCHED_QK) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) read_k_block<ST>(kb, kb);
     }
@@ -157,9 +157,13 @@ struct Bf16Fwd {
     }
   }
 
-  // K fragments in flight ahead of the MFMAs that use them, in k-steps, in
-  // the streamed 64-key tile (one k-step = two MFMAs = 64 MFMA cycles).
-  static constexpr int kKAhead = 3;
+  // K fragments in flight ahead of the MFMAs that use them, in k-steps of
+  // NKB MFMAs each (same-box sweeps of 2 .. 6: d = 128 with 64-key tiles 3,
+  // with 32-key tiles 6; d = 64: 2; d = 256: 4).
+  static constexpr int kKAhead = NKB == 2 ? (D == 64 ? 2 : 3) : (D == 256 ? 4 : 6);
+  // QK^T runs in that scheduled order for every instance with 32 queries
+  // per wave.
+  static constexpr bool SCHED_QK = QB == 1;
 
   // S^T of the tile in K stage ST.
   template <int ST>
@@ -168,13 +172,14 @@ struct Bf16Fwd {
     for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sacc[b][kb] = f32x16{};
-    if constexpr (STREAM && QB == 1 && NKB == 2) {
-      // The two 32-key blocks' accumulator chains advance together, k-step
-      // by k-step, and each step's two K fragments are read kKAhead steps
-      // before their MFMAs. Left to itself the compiler streams one block's
-      // fragments into a single register set, so each of its MFMAs waits a
-      // whole LDS round trip; this order hides the round trips (about 2% at
-      // B16 H16 N8192 in a same-box A/B, bit-identical outputs).
+    if constexpr (SCHED_QK) {
+      // The 32-key blocks' accumulator chains advance together, k-step by
+      // k-step, and each step's K fragments are read kKAhead steps before
+      // their MFMAs. Left to itself the compiler streams a block's fragments
+      // through one register set, or waits for all reads before the first
+      // MFMA, so MFMAs wait whole LDS round trips. Same-box A/B, bit-identical
+      // outputs: +2.0 .. 2.8% at B16 H16 N8192, +2 .. 2.6% causal (N 2048 and
+      // 8192), +3.9% causal window 1024 at d = 64, +3% at d = 256.
       bf16x8 f[KSTEPS][NKB];
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t)
@@ -185,12 +190,14 @@ struct Bf16Fwd {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           sacc[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[t][kb], qf[0][t], sacc[0][kb], 0, 0, 0);
-      // scheduling groups: 0x100 = LDS reads, 0x008 = MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKAhead, 0);
+      // scheduling groups (0x100 = LDS reads, 0x008 = MFMAs) take the
+      // instructions that precede them, so the V reads of an iteration come
+      // after this function
+      __builtin_amdgcn_sched_group_barrier(0x100, NKB * kKAhead, 0);
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (t + kKAhead < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NKB, 0);
+        if (t + kKAhead < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
       }
       return;
     }
@@ -353,8 +360,9 @@ struct Bf16Fwd {
     issue_k<PB ^ 1>(j + 1);
     issue_v<PB>(j);
     read_k<PB>();
-    if constexpr (!FIRST) read_v<PB ^ 1>();
+    if constexpr (!FIRST && !SCHED_QK) read_v<PB ^ 1>();
     qk<PB>();
+    if constexpr (!FIRST && SCHED_QK) read_v<PB ^ 1>();
     rescale();
     if constexpr (!FIRST) pv<PB ^ 1>();
     softmax<EDGE, PB, FIRST>(j);
