@@ -166,24 +166,6 @@ struct Fp8Fwd {
                     (int)((uint32_t)kt * VTILE + u * 16 * kThreads));
   }
 
-  // A operand of S^T = K Q^T for 32-key block kb. E4M3: lane holds
-  // K8[32 kb + l32][64 t + 32 h .. +31]; bf16: K[32 kb + l32][16 t + 8 h .. +7].
-  template <int ST>
-  __device__ __forceinline__ void read_k(int kb, const int (&ko)[KSTEPS][2]) {
-    const lds_char* Ks = kl[ST];
-    const int row = kb * 32 + l32;
-#pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-      if constexpr (QBF) {
-        const int ch = 2 * t + h;
-        kf[kb][t] = *(const lds_bf16x8*)(Ks + row * D * 2 + ((ch ^ bf16_swz_k<D>(row)) << 4));
-      } else {
-        const i32x4 a0 = *(const lds_i32x4*)(Ks + kb * 32 * D + ko[t][0]);
-        const i32x4 a1 = *(const lds_i32x4*)(Ks + kb * 32 * D + ko[t][1]);
-        kf[kb][t] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      }
-    }
-  }
   // A operand of O^T += V^T P^T for the 64-key half hh: lane (d, h) reads LDS
   // rows 64 hh + 16t + 8h .. +7 of column d for t = 0..3 (the swapped key
   // order makes these its P's keys).
@@ -205,28 +187,24 @@ struct Fp8Fwd {
     }
   }
 
-  // S^T of 32-key block kb.
-  __device__ __forceinline__ void qk(int kb) {
-    sacc[kb] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-      if constexpr (QBF)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][t], qf[t], sacc[kb], 0, 0, 0);
-      else
-        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[kb][t], qf[t], sacc[kb], 0, 0,
-                                                                   0, 0, 0, 0);
-    }
-  }
-  // K fragments and S^T of the whole tile, read and multiplied one 32-key
-  // block at a time, so only one block of fragments is live.
-  // E4M3 K: lane reads chunks 4t + 2h and 4t + 2h + 1 of row 32 kb + l32.
-  // Rows 32 kb + l32 share the swizzle of l32 (it reads row bits 0..3), so
-  // block kb is a constant offset. The four chunk addresses are rebuilt every
-  // tile from two registers (one v_bitop3 each: krow has no bits where the
-  // chunk index sits) rather than kept live across the loop, where they would
-  // be spilled; the empty asm stops the compiler from hoisting them.
+  // K fragments (A operand of S^T = K Q^T for 32-key block kb) and S^T of
+  // the whole tile. The blocks' accumulator chains advance together, k-step
+  // by k-step, and scheduling groups (0x100 = LDS reads, 0x008 = MFMAs) keep
+  // the fragment reads a fixed distance ahead of the MFMAs that use them;
+  // left to itself the compiler streams a block through one register set and
+  // each MFMA waits a whole LDS round trip. The groups take the LDS reads that
+  // precede them, so the caller issues its V reads after this function.
+  // bf16 K: lane holds K[32 kb + l32][16 t + 8 h .. +7].
+  // E4M3 K: lane holds K8[32 kb + l32][64 t + 32 h .. +31], chunks 4t + 2h
+  // and 4t + 2h + 1 of its row. Rows 32 kb + l32 share the swizzle of l32 (it
+  // reads row bits 0..3), so block kb is a constant offset. The four chunk
+  // addresses are rebuilt every tile from two registers (one v_bitop3 each:
+  // krow has no bits where the chunk index sits) rather than kept live across
+  // the loop, where they would be spilled; the empty asm stops the compiler
+  // from hoisting them.
   template <int ST>
   __device__ __forceinline__ void read_k_qk() {
+    static_assert(!QBF || NKB == 2, "bf16-score tiles hold two 32-key blocks");
     int ko[KSTEPS][2] = {};
     if constexpr (!QBF) {
       int sw = kswz;
@@ -238,13 +216,9 @@ struct Fp8Fwd {
         ko[t][1] = krow | (((ch + 1) << 4) ^ sw);
       }
     }
-    if constexpr (QBF && NKB == 2) {
-      // bf16 scores in 64-key tiles: the two blocks' accumulator chains
-      // advance together, k-step by k-step, with each step's two fragments
-      // read kKAhead steps before their MFMAs (scheduling groups: 0x100 = LDS
-      // reads, 0x008 = MFMAs). Left to itself the compiler streams block 0
-      // through one register set and each of its MFMAs waits a whole LDS
-      // round trip (+1.1% at B16 H16 N8192 in a same-box A/B, bit-identical).
+    if constexpr (QBF) {
+      // each step's two fragments read three steps ahead (+1.1% at B16 H16
+      // N8192 in a same-box A/B, bit-identical)
       bf16x8 f[KSTEPS][NKB];
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t)
@@ -268,12 +242,34 @@ struct Fp8Fwd {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         if (t + kKAhead < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      return;
-    }
+    } else {
+      // each fragment (two 16-byte reads) read kE8Ahead MFMAs ahead
+      // (same-box A/B, bit-identical: +1.6 .. 2.1% at d = 128 with one MFMA
+      // ahead, +1% at d = 64 with two)
+      constexpr int kE8Ahead = D == 64 ? 2 : 1;
+      i32x8 f[KSTEPS][NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      read_k<ST>(kb, ko);
-      qk(kb);
+      for (int t = 0; t < KSTEPS; ++t)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const i32x4 a0 = *(const lds_i32x4*)(kl[ST] + kb * 32 * D + ko[t][0]);
+          const i32x4 a1 = *(const lds_i32x4*)(kl[ST] + kb * 32 * D + ko[t][1]);
+          f[t][kb] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[t][kb], qf[t], sacc[kb], 0, 0,
+                                                                     0, 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kE8Ahead, 0);
+#pragma unroll
+      for (int i = 0; i < KSTEPS * NKB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + kE8Ahead < KSTEPS * NKB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
     }
   }
 
