@@ -65,12 +65,43 @@ KERNEL_SOURCES = {
 }
 
 
+def strip_c_comments(text: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed to one
+    space (string and character literals kept as they are), so that editing a
+    comment does not change the hash of the code a measurement was taken on."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def kernel_source_hash(kind: str = "bf16") -> str:
+    """Hash of the code (comments and layout stripped from the C/C++ files;
+    the build script as it is) that the kernel of one kind is compiled from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_attention_forward_attn_amd", "csrc")
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        if not f.endswith(".py"):
+            text = strip_c_comments(text)
+        h.update((f + "\0" + text).encode())
     return h.hexdigest()[:16]
 
 

@@ -74,3 +74,29 @@ def test_kernel_source_hash_tracks_the_sources():
     assert len(h) == 16 and int(h, 16) >= 0
     assert bench.kernel_source_hash("bf16") == h
     assert bench.kernel_source_hash("fp8") != h
+
+
+def test_strip_c_comments_keeps_code_and_literals():
+    src = 'int a = 1; // note\n/* block\n comment */ const char* s = "a // b /* c */";\nchar q = \'"\';  int  b;\n'
+    assert bench.strip_c_comments(src) == 'int a = 1; const char* s = "a // b /* c */"; char q = \'"\'; int b;'
+    # an escaped quote inside a literal does not end it
+    assert bench.strip_c_comments('x = "a\\" // b"; // c') == 'x = "a\\" // b";'
+
+
+def test_kernel_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    csrc = tmp_path / "tiled_attention_forward_attn_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    src_root = os.path.join(ROOT, "tiled_attention_forward_attn_amd")
+    for f in bench.KERNEL_SOURCES["bf16"]:
+        path = os.path.normpath(os.path.join(src_root, "csrc", f))
+        dst = os.path.normpath(os.path.join(str(csrc), f))
+        with open(path) as fh, open(dst, "w") as out:
+            out.write(fh.read())
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash("bf16")
+    main = csrc / "attn_fwd_bf16.hip"
+    text = main.read_text()
+    main.write_text("// an added comment line\n" + text.replace("\n", "\n\n", 3))
+    assert bench.kernel_source_hash("bf16") == h0
+    main.write_text(text.replace("kRescaleSlack = 8.f", "kRescaleSlack = 7.f"))
+    assert bench.kernel_source_hash("bf16") != h0

@@ -24,11 +24,13 @@
 //    ping-pong buffers, [WGC]'s prefetch of the next KV block). The barrier
 //    between tiles carries no memory fence, so those copies stay in flight.
 //  * Software pipeline inside the wave ([JJ] section 2.2, GEMM/softmax
-//    overlap). Iteration j: read all K_j and V_{j-1} fragments of the tile
-//    from LDS up front (their latency hides behind the MFMAs), issue the
-//    MFMAs of S(j) = K_j Q^T, then the MFMAs of O += P(j-1) V_{j-1}
+//    overlap). Iteration j: the MFMAs of S(j) = K_j Q^T, with each K fragment
+//    read from LDS a fixed number of k-steps ahead of its MFMA (scheduling
+//    groups), then the V_{j-1} fragments and the MFMAs of O += P(j-1) V_{j-1}
 //    interleaved with the softmax of S(j), so the exponentials run while the
-//    matrix cores are busy. P alternates between two register sets.
+//    matrix cores are busy (interleaving independent VALU work into a wave's
+//    own MFMA stream is what the SIMD overlaps; a VALU-only wave beside an
+//    MFMA-only wave is not). P alternates between two register sets.
 //  * Online softmax in base 2 with log2(e) folded into the scale (v_exp_f32
 //    computes 2^x). A tile is first exponentiated against the row's current
 //    reference max; only if some lane's sum of p exceeds a bound (first tile,
@@ -86,10 +88,11 @@ struct Bf16Fwd {
   f32x16 oacc[QB][DBLK];
   f32x16 sacc[QB][NKB];
   bf16x8 pbuf[2][QB][PST];
-  // Fragments streamed from LDS right before their MFMAs: the 64-key tile at
-  // d = 128 holds one 32-key block of K fragments and one 16-key step of V
-  // fragments at a time (all of a tile's would not fit two waves per SIMD).
-  // Otherwise a tile's K and V fragments are all read up front.
+  // V fragments of the 64-key tile at d = 128 are streamed from LDS one
+  // 16-key step at a time, right before their MFMAs (a whole tile's would not
+  // fit two waves per SIMD); other tiles read theirs together. K fragments go
+  // through the scheduled QK^T (qk) with 32 queries per wave; the kf sets
+  // serve the general form for more queries per wave.
   static constexpr bool STREAM = D == 128 && BN == 64;
   bf16x8 kf[STREAM ? 1 : NKB][KSTEPS];
   bf16x8 vf[STREAM ? 1 : PST][DBLK];
