@@ -181,8 +181,9 @@ struct Bf16Fwd {
       // their MFMAs. Left to itself the compiler streams a block's fragments
       // through one register set, or waits for all reads before the first
       // MFMA, so MFMAs wait whole LDS round trips. Same-box A/B, bit-identical
-      // outputs: +2.0 .. 2.8% at B16 H16 N8192, +2 .. 2.6% causal (N 2048 and
-      // 8192), +3.9% causal window 1024 at d = 64, +3% at d = 256.
+      // outputs: +2.0 .. 2.8% at B16 H16 N8192, +4.4% causal B4 H16 N2048,
+      // +2.5% causal B16 H16 N8192, +3.9 .. 4.2% causal window 1024 at d = 64,
+      // +2.7 .. 3% at d = 256.
       bf16x8 f[KSTEPS][NKB];
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t)
