@@ -390,6 +390,52 @@ def bench_fp8(tafa, dev, steps, warmup, stream):
     return res
 
 
+SWEEP_TOKENS = 131072          # B * N of every sweep point
+SWEEP_N = [512, 1024, 2048, 4096, 8192, 16384, 32768]
+
+
+def run_sweep(tafa, torch, stream):
+    """Throughput across sequence lengths at a constant number of tokens per
+    batch (B = 131072 / N; H = 32, 16, 8 at d = 64, 128, 256), causal and not,
+    for bf16, all-E4M3 fp8 and the fp8 PV mode. Timing only: the inputs are
+    seeded normal values drawn on the device (parity is the tests' job).
+    Prints a markdown table: TFLOP/s and the fraction of the dense peak of the
+    MFMA type that does the work (the PV mode against its mixed ceiling)."""
+    gen = torch.Generator(device="cuda:0")
+    kinds = [("bf16", 64), ("bf16", 128), ("bf16", 256), ("fp8", 64), ("fp8", 128), ("fp8pv", 128)]
+    print("| kind | d | N | B | H | causal | ms per launch | TFLOP/s | fraction of peak |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for kind, d in kinds:
+        H = {64: 32, 128: 16, 256: 8}[d]
+        peak = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "fp8pv": PEAK_MIXED_TFLOPS}[kind]
+        for N in SWEEP_N:
+            B = SWEEP_TOKENS // N
+            gen.manual_seed(N * 1000 + d)
+            q, k, v = [torch.randn(B, H, N, d, generator=gen, device="cuda:0").to(torch.bfloat16)
+                       for _ in range(3)]
+            descales = None
+            if kind == "fp8":
+                (q, dq), (k, dk), (v, dv) = [tafa.quantize(t) for t in (q, k, v)]
+                descales = (dq, dk, dv)
+            elif kind == "fp8pv":
+                v, dv = tafa.quantize(v)
+                descales = (None, None, dv)
+            o = torch.empty(B, H, N, d, dtype=torch.bfloat16, device="cuda:0")
+            lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda:0")
+            for causal in (False, True):
+                def launch():
+                    tafa.fwd(q, k, v, causal=causal, descales=descales, out=o, lse=lse)
+                one = time_grouped(launch, 1, 3, 2, stream)[0]
+                per_group = max(3, min(200, int(20.0 / max(one, 1e-3))))
+                ms = min(time_grouped(launch, 5, per_group, 2, stream))
+                flop = 4.0 * d * allowed_pairs(N, causal, -1) * B * H
+                tf = flop / (ms * 1e-3) / 1e12
+                print(f"| {kind} | {d} | {N} | {B} | {H} | {int(causal)} | {ms:.4f} | {tf:.1f} | "
+                      f"{tf / peak:.3f} |", flush=True)
+            del q, k, v, o, lse
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +447,9 @@ def main():
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-d256", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only print a markdown table of throughput across sequence lengths "
+                         "(bf16 d 64/128/256, fp8, fp8 PV mode; causal and not)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -426,6 +475,9 @@ def main():
     tafa.load()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if args.sweep:
+        run_sweep(tafa, torch, stream)
+        return
 
     w = BY_NAME[DEFAULT_WORKLOAD]
     flop = workload_flop(w)
