@@ -90,11 +90,9 @@ struct Bf16Fwd {
   bf16x8 pbuf[2][QB][PST];
   // V fragments of the 64-key tile at d = 128 are streamed from LDS one
   // 16-key step at a time, right before their MFMAs (a whole tile's would not
-  // fit two waves per SIMD); other tiles read theirs together. K fragments go
-  // through the scheduled QK^T (qk) with 32 queries per wave; the kf sets
-  // serve the general form for more queries per wave.
+  // fit two waves per SIMD); other tiles read theirs together. K fragments are
+  // read inside the scheduled QK^T (qk).
   static constexpr bool STREAM = D == 128 && BN == 64;
-  bf16x8 kf[STREAM ? 1 : NKB][KSTEPS];
   bf16x8 vf[STREAM ? 1 : PST][DBLK];
   float m[QB], l[QB], alpha[QB];
   bool owe_rescale;
@@ -119,18 +117,6 @@ struct Bf16Fwd {
     const int row = kb * 32 + l32;
     const int ch = 2 * t + h;
     return *(const lds_bf16x8*)(kl[ST] + row * D * 2 + ((ch ^ bf16_swz_k<D>(row)) << 4));
-  }
-  template <int ST>
-  __device__ __forceinline__ void read_k_block(int kb, int i) {
-#pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) kf[i][t] = k_frag<ST>(kb, t);
-  }
-  template <int ST>
-  __device__ __forceinline__ void read_k() {
-    if constexpr (!STREAM && !SCHED_QK) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) read_k_block<ST>(kb, kb);
-    }
   }
   // A operand of O^T += V^T P^T for MFMA step s (into fragment set i): lane
   // (d, h) holds V at keys 16 s + 4 h + 0..3 and + 8 (the key order of the
@@ -161,12 +147,9 @@ struct Bf16Fwd {
   }
 
   // K fragments in flight ahead of the MFMAs that use them, in k-steps of
-  // NKB MFMAs each (same-box sweeps of 2 .. 6: d = 128 with 64-key tiles 3,
-  // with 32-key tiles 6; d = 64: 2; d = 256: 4).
+  // NKB QB MFMAs each (same-box sweeps of 2 .. 6 with QB = 1: d = 128 with
+  // 64-key tiles 3, with 32-key tiles 6; d = 64: 2; d = 256: 4).
   static constexpr int kKAhead = NKB == 2 ? (D == 64 ? 2 : 3) : (D == 256 ? 4 : 6);
-  // QK^T runs in that scheduled order for every instance with 32 queries
-  // per wave.
-  static constexpr bool SCHED_QK = QB == 1;
 
   // S^T of the tile in K stage ST.
   template <int ST>
@@ -175,45 +158,34 @@ struct Bf16Fwd {
     for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sacc[b][kb] = f32x16{};
-    if constexpr (SCHED_QK) {
-      // The 32-key blocks' accumulator chains advance together, k-step by
-      // k-step, and each step's K fragments are read kKAhead steps before
-      // their MFMAs. Left to itself the compiler streams a block's fragments
-      // through one register set, or waits for all reads before the first
-      // MFMA, so MFMAs wait whole LDS round trips. Same-box A/B, bit-identical
-      // outputs: +2.0 .. 2.8% at B16 H16 N8192, +4.4% causal B4 H16 N2048,
-      // +2.5% causal B16 H16 N8192, +3.9 .. 4.2% causal window 1024 at d = 64,
-      // +2.7 .. 3% at d = 256.
-      bf16x8 f[KSTEPS][NKB];
+    // The 32-key blocks' accumulator chains advance together, k-step by
+    // k-step, and each step's K fragments are read kKAhead steps before their
+    // MFMAs. Left to itself the compiler streams a block's fragments through
+    // one register set, or waits for all reads before the first MFMA, so
+    // MFMAs wait whole LDS round trips. Same-box A/B, bit-identical outputs:
+    // +2.0 .. 2.8% at B16 H16 N8192, +4.4% causal B4 H16 N2048, +2.5% causal
+    // B16 H16 N8192, +3.9 .. 4.2% causal window 1024 at d = 64, +2.7 .. 3% at
+    // d = 256.
+    bf16x8 f[KSTEPS][NKB];
 #pragma unroll
-      for (int t = 0; t < KSTEPS; ++t)
+    for (int t = 0; t < KSTEPS; ++t)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) f[t][kb] = k_frag<ST>(kb, t);
+      for (int kb = 0; kb < NKB; ++kb) f[t][kb] = k_frag<ST>(kb, t);
 #pragma unroll
-      for (int t = 0; t < KSTEPS; ++t)
+    for (int t = 0; t < KSTEPS; ++t)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          sacc[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[t][kb], qf[0][t], sacc[0][kb], 0, 0, 0);
-      // scheduling groups (0x100 = LDS reads, 0x008 = MFMAs) take the
-      // instructions that precede them, so the V reads of an iteration come
-      // after this function
-      __builtin_amdgcn_sched_group_barrier(0x100, NKB * kKAhead, 0);
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, NKB, 0);
-        if (t + kKAhead < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
-      }
-      return;
-    }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      if constexpr (STREAM) read_k_block<ST>(kb, 0);
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int b = 0; b < QB; ++b)
-          sacc[b][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[STREAM ? 0 : kb][t], qf[b][t],
-                                                                sacc[b][kb], 0, 0, 0);
+          sacc[b][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[t][kb], qf[b][t], sacc[b][kb], 0, 0, 0);
+    // scheduling groups (0x100 = LDS reads, 0x008 = MFMAs) take the
+    // instructions that precede them, so the V reads of an iteration come
+    // after this function
+    __builtin_amdgcn_sched_group_barrier(0x100, NKB * kKAhead, 0);
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NKB * QB, 0);
+      if (t + kKAhead < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
     }
   }
 
@@ -363,10 +335,8 @@ struct Bf16Fwd {
     // rows past N read as zero through the buffer range check.
     issue_k<PB ^ 1>(j + 1);
     issue_v<PB>(j);
-    read_k<PB>();
-    if constexpr (!FIRST && !SCHED_QK) read_v<PB ^ 1>();
     qk<PB>();
-    if constexpr (!FIRST && SCHED_QK) read_v<PB ^ 1>();
+    if constexpr (!FIRST) read_v<PB ^ 1>();
     rescale();
     if constexpr (!FIRST) pv<PB ^ 1>();
     softmax<EDGE, PB, FIRST>(j);
