@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--no-fp8] [--no-configs] [--no-merge] [--no-decode] [--no-d256]
+    python bench.py --sweep | --gemm-calibration | --copy-calibration
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 one bf16 attn_fwd launch over B16 H16 N8192 d128 (non-causal), the headline
@@ -436,6 +437,45 @@ def run_sweep(tafa, torch, stream):
             torch.cuda.empty_cache()
 
 
+def gemm_calibration(tafa, torch, stream):
+    """The rate of the platform's library GEMM (hipBLASLt through torch) on
+    large square products, bf16 and E4M3, beside the headline attention in
+    the same process: a same-box reference for what an LDS-fed MFMA kernel
+    reaches at the clock the part holds under load. The bf16 product uses the
+    layout hipBLASLt runs fastest here (second operand stored transposed, as
+    F.linear passes it); E4M3 runs through torch._scaled_mm with unit scales.
+    Prints one JSON line."""
+    import torch.nn.functional as F
+    from attn_inputs import BY_NAME, workload_qkv
+    gen = torch.Generator(device="cuda:0")
+    out = {"note": "library GEMM (hipBLASLt via torch), for context; not part of the product path"}
+    for n in (8192, 16384):
+        gen.manual_seed(n)
+        a = torch.randn(n, n, generator=gen, device="cuda:0").to(torch.bfloat16)
+        w = torch.randn(n, n, generator=gen, device="cuda:0").to(torch.bfloat16)
+        flop = 2.0 * n ** 3
+        ms = min(time_grouped(lambda: F.linear(a, w), 3, 10, 2, stream))
+        out[f"bf16_gemm_{n}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+        a8, w8 = a.to(torch.float8_e4m3fn), w.to(torch.float8_e4m3fn)
+        one = torch.ones((), device="cuda:0")
+        ms = min(time_grouped(lambda: torch._scaled_mm(a8, w8.t(), scale_a=one, scale_b=one,
+                                                       out_dtype=torch.bfloat16), 3, 10, 2, stream))
+        out[f"fp8_gemm_{n}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+        del a, w, a8, w8
+        torch.cuda.empty_cache()
+    wl = BY_NAME[DEFAULT_WORKLOAD]
+    q, k, v = workload_qkv(wl, device=torch.device("cuda:0"))
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device="cuda:0")
+    ms = min(time_grouped(lambda: tafa.fwd(q, k, v, causal=wl.causal, window=wl.window,
+                                           scale=wl.scale, out=o, lse=lse), 3, 5, 2, stream))
+    att = workload_flop(wl) / (ms * 1e-3) / 1e12
+    best = max(out["bf16_gemm_8192_tflops"], out["bf16_gemm_16384_tflops"])
+    out[f"attention_{wl.name}_tflops"] = round(att, 1)
+    out["attention_over_best_bf16_gemm"] = round(att / best, 3)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -450,6 +490,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="only print a markdown table of throughput across sequence lengths "
                          "(bf16 d 64/128/256, fp8, fp8 PV mode; causal and not)")
+    ap.add_argument("--gemm-calibration", action="store_true",
+                    help="only time the library GEMM (bf16 and E4M3, 8192^3 and 16384^3) beside "
+                         "the headline attention, for context; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -477,6 +520,9 @@ def main():
     stream = torch.cuda.current_stream()
     if args.sweep:
         run_sweep(tafa, torch, stream)
+        return
+    if args.gemm_calibration:
+        gemm_calibration(tafa, torch, stream)
         return
 
     w = BY_NAME[DEFAULT_WORKLOAD]
