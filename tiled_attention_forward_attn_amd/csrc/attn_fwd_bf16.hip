@@ -93,6 +93,7 @@ struct Bf16Fwd {
   // fit two waves per SIMD); other tiles read theirs together. K fragments are
   // read inside the scheduled QK^T (qk).
   static constexpr bool STREAM = D == 128 && BN == 64;
+  static constexpr bool kRescaleFirst = D == 256;
   bf16x8 vf[STREAM ? 1 : PST][DBLK];
   float m[QB], l[QB], alpha[QB];
   bool owe_rescale;
@@ -335,9 +336,15 @@ struct Bf16Fwd {
     // rows past N read as zero through the buffer range check.
     issue_k<PB ^ 1>(j + 1);
     issue_v<PB>(j);
+    // At d = 256 (one workgroup per CU, registers to spare) the owed rescale
+    // goes first, so QK^T, the V reads and PV share one scheduling region and
+    // the V reads start under the QK^T MFMAs (+1.8% in a same-box A/B,
+    // bit-identical). Elsewhere the V fragments this keeps live cost more
+    // than the earlier reads gain (-2% at B16 H16 N8192 d128).
+    if constexpr (kRescaleFirst) rescale();
     qk<PB>();
     if constexpr (!FIRST) read_v<PB ^ 1>();
-    rescale();
+    if constexpr (!kRescaleFirst) rescale();
     if constexpr (!FIRST) pv<PB ^ 1>();
     softmax<EDGE, PB, FIRST>(j);
     __builtin_amdgcn_iglp_opt(0);
